@@ -1,0 +1,167 @@
+/*
+ * libdpnorm: randomized per-sample gradient-norm estimation on MI355X (gfx950).
+ *
+ * The operations follow "Efficient DP-SGD for LLMs with Randomized Clipping"
+ * (papernotes.org ICML 2026 note; gist.science/nl technical summary):
+ *   - for a linear-like layer with hooked activations A_i (T x d) and output
+ *     gradients G_i (T x p) of sample i, the squared per-sample gradient norm
+ *     is ||A_i^T G_i||_F^2 = trace(G_i^T A_i A_i^T G_i) (note: 切入角度);
+ *   - the Hutchinson estimate with a Gaussian projection P (p x k, entries of
+ *     variance 1/k) is ||A_i^T (G_i P)||_F^2 (note: 关键设计 › Hutchinson);
+ *   - Hutch++ splits the spectrum into an exact head on an orthonormal basis
+ *     Q of Col(O S) and a Hutchinson tail on (I - Q Q^T) (note: 关键设计 ›
+ *     Hutch++; summary: Kernmechanisme);
+ *   - estimates are summed over layers per sample and the clip factor is
+ *     min(C / sqrt(n_i), 1) (note: 方法详解 › 整体框架).
+ *
+ * Conventions for every entry point
+ *   Pointers named A, G, P, S, n, c, head, tail, rank, ws are DEVICE pointers
+ *   owned by the caller; the library allocates and frees nothing and keeps no
+ *   pointer after returning. Arrays of layer descriptors and trace records are
+ *   HOST memory. All work is enqueued on `stream` (0 = the null stream) and
+ *   runs asynchronously; results are valid once the stream has been
+ *   synchronised. Calls on one stream execute in order, which is what makes
+ *   accumulate = 1 a layer sum.
+ *   Layouts are row-major and contiguous: A [B][T][d], G [B][T][p],
+ *   P [p][k] (or [p][m_t] for the Hutch++ tail), S [p][m_s]; n, c, head,
+ *   tail are float [B]; rank is int32 [B]. P and S are shared by the B
+ *   samples of a call and drawn by the caller; the library has no RNG, so a
+ *   call is a deterministic function of its inputs and is bitwise
+ *   reproducible run to run.
+ *   Element types: DPNORM_BF16 (A, G, P, S bf16; products accumulate in
+ *   fp32) or DPNORM_F32 (all fp32). The widths d and p must be multiples of
+ *   8 (bf16) or 4 (fp32) so every row starts on a 16-byte boundary, and base
+ *   pointers must be 16-byte aligned. T and B are arbitrary (>= 1).
+ *   Workspace: `ws` of at least the size reported by the matching
+ *   *_workspace query (256-byte aligned); it may be NULL only when that size
+ *   is 0. Concurrent calls on different streams need distinct workspaces.
+ *   Errors: every function returns a status and never aborts or prints. The
+ *   checks below run on the host before anything is enqueued, so on error no
+ *   output has been written. NaN or Inf inside the data is not checked; it
+ *   propagates into n and c.
+ */
+#ifndef DPNORM_H
+#define DPNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef enum dpnorm_status {
+  DPNORM_OK = 0,
+  DPNORM_ERR_NULL = 1,        /* a required pointer is NULL */
+  DPNORM_ERR_SIZE = 2,        /* a size < 1, too large, misaligned width, bad budget */
+  DPNORM_ERR_DTYPE = 3,       /* unknown element type or route */
+  DPNORM_ERR_VALUE = 4,       /* C <= 0 or not finite; outputs alias inputs */
+  DPNORM_ERR_WORKSPACE = 5,   /* ws_bytes below the workspace query */
+  DPNORM_ERR_ALIGN = 6,       /* a base pointer is not 16-byte aligned (ws: 256) */
+  DPNORM_ERR_HIP = 7          /* a kernel launch or HIP call failed */
+} dpnorm_status;
+
+typedef enum dpnorm_dtype { DPNORM_F32 = 0, DPNORM_BF16 = 1 } dpnorm_dtype;
+
+typedef enum dpnorm_route {
+  DPNORM_EXACT_AUTO = 0,      /* explicit when d*p <= T*T, else Gram */
+  DPNORM_EXACT_EXPLICIT = 1,  /* sum of squares of A^T G tiles (never stored) */
+  DPNORM_EXACT_GRAM = 2       /* <A A^T, G G^T> over T x T tiles (never stored) */
+} dpnorm_route;
+
+/* One linear-like layer of a grouped call: device pointers A [B][T][d],
+ * G [B][T][p], P [p][k]. */
+typedef struct dpnorm_layer {
+  const void* A;
+  const void* G;
+  const void* P;
+  int64_t d;
+  int64_t p;
+} dpnorm_layer;
+
+/* Kernel kinds reported by the traced grouped call. */
+typedef enum dpnorm_kernel_kind {
+  DPNORM_KERNEL_PREPARE = 1,   /* layer records, work lists, P -> MFMA fragments */
+  DPNORM_KERNEL_ROWPROJ = 2,   /* G P (skinny GEMM, streams G) */
+  DPNORM_KERNEL_TCONTRACT = 3, /* A^T (G P) + squared Frobenius (streams A) */
+  DPNORM_KERNEL_YSUM = 4,      /* split-T partial sums, then squared Frobenius */
+  DPNORM_KERNEL_FINISH = 5     /* per-sample sum, layer sum, clip */
+} dpnorm_kernel_kind;
+
+/* Event trace for profiling one grouped call. `events` holds `capacity`
+ * caller-created events (dpnorm_event_create). The call records events[0]
+ * before its first launch and events[j] after its j-th launch, and sets
+ * kinds[j-1] to that launch's dpnorm_kernel_kind; `count` returns the number
+ * of events recorded. If capacity is too small, DPNORM_ERR_SIZE is returned
+ * before anything is enqueued. */
+typedef struct dpnorm_trace {
+  hipEvent_t* events;
+  int32_t* kinds;
+  int64_t capacity;
+  int64_t count;
+} dpnorm_trace;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int dpnorm_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* dpnorm_status_string(int status);
+
+/* Hutch++ budget split (note: 关键设计 › Hutch++, and the efficiency table
+ * whose Hutch++ FLOP figures correspond to equal column counts): m_s =
+ * ceil(k/3) sketch columns (and up to m_s head columns), m_t = k - 2 m_s tail
+ * columns. Returns DPNORM_ERR_SIZE when k < 3 (no tail) or k > 96. */
+dpnorm_status dpnorm_hutchpp_split(int64_t k, int64_t* m_s, int64_t* m_t);
+
+/* ---- workspace queries (host only; no device work) ---- */
+dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p,
+                                     int64_t k, size_t* bytes);
+dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
+                                             int64_t B, int64_t T, int64_t k, size_t* bytes);
+/* Hutchinson estimate of one layer (note: 关键设计 › Hutchinson; summary:
+ * Kernmechanisme item 1): n_hat_i = ||A_i^T (G_i P)||_F^2 for every sample,
+ * P [p][k] shared by the samples (caller draws N(0, 1/k) entries;
+ * 1 <= k <= 64).
+ * accumulate = 0 writes n[i] = n_hat_i; accumulate = 1 adds: n[i] += n_hat_i.
+ * A, G, P, n device pointers; n must not overlap A, G, P or ws. */
+dpnorm_status dpnorm_hutch(const void* A, const void* G, const void* P, dpnorm_dtype dt, int64_t B,
+                           int64_t T, int64_t d, int64_t p, int64_t k, float* n, int accumulate,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Hutchinson estimates of L layers summed per sample (note: 方法详解 ›
+ * 整体框架, layer sum): n[i] (+)= sum_l ||A_i^(l)T (G_i^(l) P^(l))||_F^2.
+ * Same semantics as L dpnorm_hutch calls with accumulate = 1 after the first,
+ * in fewer launches. `layers` is a host array of L >= 1 descriptors with
+ * device pointers. If c is not NULL, c[i] = min(C / sqrt(n[i]), 1) is also
+ * written from the final n (then C must be finite and > 0; c may equal n). */
+dpnorm_status dpnorm_hutch_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                   int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* dpnorm_hutch_grouped with an event trace (see dpnorm_trace). */
+dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
+                                          int64_t B, int64_t T, int64_t k, float* n, int accumulate,
+                                          float* c, float C, void* ws, size_t ws_bytes,
+                                          hipStream_t stream, dpnorm_trace* trace);
+
+/* Clip factors (note: 方法详解 › 整体框架): c[i] = min(C / sqrt(n[i]), 1),
+ * with n = 0 giving 1, n = +inf giving 0 and NaN propagating. C must be
+ * finite and > 0. c == n (in place) is allowed; other overlap is an error. */
+dpnorm_status dpnorm_clip_factors(const float* n, int64_t B, float C, float* c, hipStream_t stream);
+
+/* Thin event helpers for profiling (wrap hipEventCreate / Destroy /
+ * ElapsedTime / Synchronize); provided so bindings need only this library. */
+dpnorm_status dpnorm_event_create(hipEvent_t* ev);
+dpnorm_status dpnorm_event_destroy(hipEvent_t ev);
+dpnorm_status dpnorm_event_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms);
+dpnorm_status dpnorm_event_record(hipEvent_t ev, hipStream_t stream);
+dpnorm_status dpnorm_event_synchronize(hipEvent_t ev);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPNORM_H */

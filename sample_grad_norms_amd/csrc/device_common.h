@@ -1,0 +1,97 @@
+// Device helpers shared by the libdpnorm kernels (gfx950 / CDNA4).
+//
+// MFMA operand conventions used throughout (v_mfma_f32_16x16x32_bf16):
+//   A operand: lane l supplies 8 bf16 of row (l % 16) at K slots 8*(l/16)+j
+//   B operand: lane l supplies 8 bf16 of column (l % 16) at K slots 8*(l/16)+j
+//   C/D      : lane l holds rows 4*(l/16) + r, r = 0..3, of column (l % 16)
+// and for v_mfma_f32_16x16x4f32 one fp32 value per lane at K slot (l/16).
+// Only the pairing of A and B K slots matters for a contraction, so the
+// kernels are free to map any contraction index to a (group, element) slot
+// as long as both operands use the same map.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Round-to-nearest-even float -> bf16 bit pattern (NaN kept a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Split x into hi + lo, both bf16, with |x - hi - lo| <= 2^-17 |x| (x - hi is
+// exact in fp32 because hi is within a factor of two of x).
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 pack8(const uint32_t b[8]) {
+  return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+}
+
+// In-register transpose of an 8 x 8 block of bf16.
+// in[s] holds 8 consecutive elements (columns e = 0..7) of row s;
+// out[e] holds rows s = 0..7 of column e, row 0 in the low half of word 0.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ void transpose8x8_bf16(const uint4 in[8], uint4 out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = word(in[2 * j], w), b = word(in[2 * j + 1], w);
+      q[j] = (e & 1) ? pack_hi16(a, b) : pack_lo16(a, b);
+    }
+    out[e] = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+}
+
+// Row of a 32-row chunk that K slot (group g, element s) of a bf16 MFMA
+// operand stands for. It is chosen so that the rows a lane holds in the
+// accumulators of two stacked 16 x 16 tiles (rows 4g + r and 16 + 4g + r)
+// are exactly the rows of its K slots: a stage-1 result feeds stage 2 from
+// the lane's own registers.
+__device__ __forceinline__ int slot_row(int g, int s) { return 16 * (s >> 2) + 4 * g + (s & 3); }
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Map a linear block index to a work item so that each XCD (blocks are
+// dispatched round-robin over the 8 XCDs) walks one contiguous range of the
+// item list; neighbouring items then share their XCD's L2.
+__device__ __forceinline__ int xcd_item(uint32_t b, uint32_t n) {
+  const uint32_t x = b & 7u, j = b >> 3;
+  const uint32_t per = n >> 3, rem = n & 7u;
+  return (int)(x * per + (x < rem ? x : rem) + j);
+}
+
+}  // namespace dpn

@@ -1,0 +1,498 @@
+// libdpnorm host layer: argument checks, workspace layout and launches.
+//
+// Every estimate in the library is one or more two-stage passes
+// (V = X1 W, then Y = X2^T V with the squared Frobenius norm of Y or Y
+// itself as the result; see internal.h). The host describes the layers of a
+// pass, lays out the caller's workspace with a bump allocator (the same code
+// answers the *_workspace queries, so a query and a call always agree), and
+// enqueues: prepare launches (records, work lists, packed W), one stage-1
+// launch, one stage-2 launch, the split-T reduction when T is split, and the
+// per-sample finisher.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "dpnorm.h"
+#include "internal.h"
+
+using namespace dpn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kTargetItems = 1024;   // stage-2 work items wanted before T is split
+constexpr int kMinChunksPerSplit = 16;   // >= 512 rows per T split
+constexpr int kMaxK = 64;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    off = align_up(off);
+    const size_t o = off;
+    off += bytes;
+    return o;
+  }
+};
+
+// One layer of a two-stage pass.
+struct PassLayer {
+  const void* X1 = nullptr;
+  const void* X2 = nullptr;
+  int64_t w1 = 0, w2 = 0;
+  const void* wsrc = nullptr;   // W source, row-major [w1][ld]
+  int wsrc_type = SRC_BF16;
+  int64_t ld = 0;
+  int ncols = 0;                // valid columns of W
+  int nsamples = 1;             // 1: W shared by the batch; B: one W per sample
+  int64_t wsrc_stride_b = 0;    // source elements between samples
+  int split = 1 << 30;          // head/tail column split of the squared sums
+  float* Yout = nullptr;        // store mode destination [B][w2][NC]
+};
+
+struct PassPlan {
+  bool bf16 = true;
+  int NCB = 2, HL = 1;
+  int64_t B = 0, T = 0, Tpad = 0;
+  int nch = 0, nsplit = 1, cols2 = kColsK2Bf16, rbs = 0;
+  bool store = false;
+  size_t off_recs = 0, off_items1 = 0, off_items2 = 0, off_partials = 0;
+  std::vector<size_t> off_W, off_V, off_Yp;
+  std::vector<int> k1_begin, n1, k2_begin, n2, ubs, slot_base, n_pack;
+  int64_t total1 = 0, total2 = 0;
+  int slots = 0;
+  bool direct() const { return !store && nsplit == 1; }
+  bool needs_ysum() const { return nsplit > 1; }
+};
+
+int ncb_of(int64_t ncols) { return ncols <= 16 ? 1 : (ncols <= 32 ? 2 : 4); }
+
+size_t packed_units(const PassPlan& pl, int64_t rows) {
+  if (pl.bf16) return (size_t)((rows + 31) / 32) * pl.NCB * pl.HL * 64;  // uint4 units
+  return (size_t)((rows + 15) / 16 * 16) * 16 * pl.NCB;                   // floats
+}
+
+// Lay out one pass over `L` in the workspace. Only sizes are used.
+void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
+  const int nl = (int)L.size();
+  pl.Tpad = (pl.T + kRowsK1 - 1) / kRowsK1 * kRowsK1;
+  pl.nch = (int)((pl.T + 31) / 32);
+  pl.rbs = (int)(pl.Tpad / kRowsK1);
+  pl.cols2 = pl.bf16 ? kColsK2Bf16 : kColsK2F32;
+  const int NC = 16 * pl.NCB;
+  pl.ubs.assign(nl, 0);
+  int64_t base_items = 0;
+  for (int l = 0; l < nl; ++l) {
+    pl.ubs[l] = (int)((L[l].w2 + pl.cols2 - 1) / pl.cols2);
+    base_items += pl.B * pl.ubs[l];
+  }
+  pl.nsplit = 1;
+  if (base_items < kTargetItems) {
+    const int max_split = std::max(1, pl.nch / kMinChunksPerSplit);
+    const int64_t want = (kTargetItems + base_items - 1) / base_items;
+    pl.nsplit = (int)std::min<int64_t>(want, max_split);
+  }
+  // stage-1 items, largest rows first so the launch ends on short items
+  std::vector<int> order(nl);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return L[a].w1 > L[b].w1; });
+  pl.k1_begin.assign(nl, 0);
+  pl.n1.assign(nl, 0);
+  pl.total1 = 0;
+  for (int l : order) {
+    pl.k1_begin[l] = (int)pl.total1;
+    pl.n1[l] = (int)(pl.B * pl.rbs);
+    pl.total1 += pl.n1[l];
+  }
+  pl.k2_begin.assign(nl, 0);
+  pl.n2.assign(nl, 0);
+  pl.slot_base.assign(nl, 0);
+  pl.n_pack.assign(nl, 0);
+  pl.total2 = 0;
+  pl.slots = 0;
+  for (int l = 0; l < nl; ++l) {
+    pl.k2_begin[l] = (int)pl.total2;
+    pl.n2[l] = (int)(pl.B * pl.ubs[l] * pl.nsplit);
+    pl.total2 += pl.n2[l];
+    pl.slot_base[l] = pl.slots;
+    pl.slots += pl.ubs[l];
+    pl.n_pack[l] = (int)(L[l].nsamples * packed_units(pl, L[l].w1));
+  }
+  pl.off_recs = bump.take(sizeof(LayerRec) * nl);
+  pl.off_items1 = bump.take(sizeof(int4) * pl.total1);
+  pl.off_items2 = bump.take(sizeof(int4) * pl.total2);
+  pl.off_partials = bump.take(sizeof(double2) * pl.B * pl.slots);
+  pl.off_W.assign(nl, 0);
+  pl.off_V.assign(nl, 0);
+  pl.off_Yp.assign(nl, 0);
+  const size_t unit = pl.bf16 ? 16 : 4;
+  for (int l = 0; l < nl; ++l) {
+    pl.off_W[l] = bump.take(unit * (size_t)pl.n_pack[l]);
+    pl.off_V[l] = bump.take((size_t)pl.B * pl.Tpad * NC * 4);
+    if (pl.nsplit > 1) pl.off_Yp[l] = bump.take((size_t)pl.nsplit * pl.B * L[l].w2 * NC * 4);
+  }
+}
+
+int pass_launches(const PassPlan& pl, int nl) {
+  return (nl + kPrepChunk - 1) / kPrepChunk + 2 + (pl.needs_ysum() ? 1 : 0);
+}
+
+// Optional event trace around each launch.
+struct Tracer {
+  dpnorm_trace* t = nullptr;
+  hipStream_t s = nullptr;
+  hipError_t begin() {
+    if (!t) return hipSuccess;
+    t->count = 1;
+    return hipEventRecord(t->events[0], s);
+  }
+  hipError_t mark(int kind) {
+    if (!t) return hipSuccess;
+    t->kinds[t->count - 1] = kind;
+    return hipEventRecord(t->events[t->count++], s);
+  }
+};
+
+#define DPN_TRY(expr)                              \
+  do {                                             \
+    const hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return e_;               \
+  } while (0)
+
+hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, hipStream_t s,
+                    Tracer& tr) {
+  const int nl = (int)L.size();
+  const int NC = 16 * pl.NCB;
+  (void)NC;
+  LayerRec* recs = (LayerRec*)(base + pl.off_recs);
+  int4* items1 = (int4*)(base + pl.off_items1);
+  int4* items2 = (int4*)(base + pl.off_items2);
+  for (int c0 = 0; c0 < nl; c0 += kPrepChunk) {
+    PrepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.recs = recs;
+    a.items1 = items1;
+    a.items2 = items2;
+    a.NCB = pl.NCB;
+    a.HL = pl.HL;
+    a.f32_target = pl.bf16 ? 0 : 1;
+    a.rbs = pl.rbs;
+    a.nsplit = pl.nsplit;
+    int units = 0;
+    const int cn = std::min(kPrepChunk, nl - c0);
+    for (int j = 0; j < cn; ++j) {
+      const int l = c0 + j;
+      const PassLayer& in = L[l];
+      PrepLayer& P = a.L[j];
+      LayerRec& R = P.rec;
+      R.X1 = in.X1;
+      R.X2 = in.X2;
+      R.W = base + pl.off_W[l];
+      R.V = base + pl.off_V[l];
+      R.Ypart = pl.nsplit > 1 ? (float*)(base + pl.off_Yp[l]) : (pl.store ? in.Yout : nullptr);
+      R.Yout = in.Yout;
+      R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
+      R.w1 = (int32_t)in.w1;
+      R.w2 = (int32_t)in.w2;
+      R.slot_base = pl.slot_base[l];
+      R.split = in.split;
+      P.wsrc = in.wsrc;
+      P.wsrc_stride_b = in.wsrc_stride_b;
+      P.wsrc_type = in.wsrc_type;
+      P.ld = (int32_t)in.ld;
+      P.ncols = in.ncols;
+      P.nsamples = in.nsamples;
+      P.layer = l;
+      P.unit_begin = units;
+      P.n_pack = pl.n_pack[l];
+      P.k1_begin = pl.k1_begin[l];
+      P.n1 = pl.n1[l];
+      P.k2_begin = pl.k2_begin[l];
+      P.n2 = pl.n2[l];
+      P.ubs = pl.ubs[l];
+      units += P.n_pack + P.n1 + P.n2 + 1;
+    }
+    a.nlayers = cn;
+    a.total_units = units;
+    DPN_TRY(launch_prepare(a, s));
+    DPN_TRY(tr.mark(DPNORM_KERNEL_PREPARE));
+  }
+  StageArgs st;
+  st.recs = recs;
+  st.B = (int32_t)pl.B;
+  st.T = (int32_t)pl.T;
+  st.Tpad = (int32_t)pl.Tpad;
+  st.nsplit = pl.nsplit;
+  st.slots_per_sample = pl.slots;
+  st.partials = (double2*)(base + pl.off_partials);
+
+  st.items = items1;
+  st.n_items = (int32_t)pl.total1;
+  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, s));
+  DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
+
+  st.items = items2;
+  st.n_items = (int32_t)pl.total2;
+  DPN_TRY(launch_tcontract(st, pl.bf16, pl.NCB, pl.direct(), s));
+  DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
+
+  if (pl.needs_ysum()) {
+    DPN_TRY(launch_ysum(st, pl.NCB, pl.cols2, pl.store ? MODE_STORE : MODE_SQ, s));
+    DPN_TRY(tr.mark(DPNORM_KERNEL_YSUM));
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks
+// ---------------------------------------------------------------------------
+size_t esize(dpnorm_dtype dt) { return dt == DPNORM_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dt) { return dt == DPNORM_F32 || dt == DPNORM_BF16; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Shape limits shared by the estimators: sizes >= 1, widths multiples of the
+// 16-byte row granule, every index used on the device fits its type.
+dpnorm_status check_dims(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p) {
+  if (B < 1 || T < 1 || d < 1 || p < 1) return DPNORM_ERR_SIZE;
+  const int64_t g = dt == DPNORM_BF16 ? 8 : 4;
+  if (d % g != 0 || p % g != 0) return DPNORM_ERR_SIZE;
+  const int64_t lim = (int64_t)1 << 30;
+  if (T > lim || d > lim || p > lim || B > lim) return DPNORM_ERR_SIZE;
+  const int64_t Tpad = (T + kRowsK1 - 1) / kRowsK1 * kRowsK1;
+  if (B > ((int64_t)1 << 31) / Tpad) return DPNORM_ERR_SIZE;   // B * Tpad < 2^31
+  const int64_t w = std::max(d, p);
+  if (T > INT64_MAX / w / B / 4) return DPNORM_ERR_SIZE;       // byte sizes fit int64
+  return DPNORM_OK;
+}
+
+dpnorm_status check_C(float C) {
+  if (!(C > 0.f) || !std::isfinite(C)) return DPNORM_ERR_VALUE;
+  return DPNORM_OK;
+}
+
+dpnorm_status hip_status(hipError_t e) { return e == hipSuccess ? DPNORM_OK : DPNORM_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// Hutchinson (grouped; a single layer is a group of one)
+// ---------------------------------------------------------------------------
+struct HutchCall {
+  PassPlan plan;
+  std::vector<PassLayer> layers;
+  size_t bytes = 0;
+};
+
+dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
+                          bool need_ptrs, HutchCall& hc) {
+  if (!layers) return DPNORM_ERR_NULL;
+  if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
+  if (L < 1 || L > (1 << 20)) return DPNORM_ERR_SIZE;
+  if (k < 1 || k > kMaxK) return DPNORM_ERR_SIZE;
+  hc.layers.resize(L);
+  int64_t items1 = 0, items2 = 0;
+  for (int64_t l = 0; l < L; ++l) {
+    const dpnorm_layer& y = layers[l];
+    const dpnorm_status st = check_dims(dt, B, T, y.d, y.p);
+    if (st != DPNORM_OK) return st;
+    if (need_ptrs) {
+      if (!y.A || !y.G || !y.P) return DPNORM_ERR_NULL;
+      if (!aligned(y.A, 16) || !aligned(y.G, 16) || !aligned(y.P, esize(dt))) return DPNORM_ERR_ALIGN;
+    }
+    PassLayer& pl = hc.layers[l];
+    pl.X1 = y.G;
+    pl.X2 = y.A;
+    pl.w1 = y.p;
+    pl.w2 = y.d;
+    pl.wsrc = y.P;
+    pl.wsrc_type = dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32;
+    pl.ld = k;
+    pl.ncols = (int)k;
+    items1 += B * ((T + kRowsK1 - 1) / kRowsK1);
+    items2 += B * ((y.d + kColsK2F32 - 1) / kColsK2F32) * 64;
+  }
+  if (items1 >= ((int64_t)1 << 31) || items2 >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;
+  PassPlan& p = hc.plan;
+  p.bf16 = dt == DPNORM_BF16;
+  p.NCB = ncb_of(k);
+  p.HL = 1;  // P is an input of the call's own element type: exact in bf16
+  p.B = B;
+  p.T = T;
+  p.store = false;
+  Bump bump;
+  plan_pass(p, hc.layers, bump);
+  hc.bytes = align_up(bump.off);
+  return DPNORM_OK;
+}
+
+dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
+                         float* n, int accumulate, float* c, float C, void* ws, size_t ws_bytes, hipStream_t stream,
+                         dpnorm_trace* trace) {
+  HutchCall hc;
+  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, hc);
+  if (st != DPNORM_OK) return st;
+  if (!n) return DPNORM_ERR_NULL;
+  if (accumulate != 0 && accumulate != 1) return DPNORM_ERR_VALUE;
+  if (!aligned(n, 4) || (c && !aligned(c, 4))) return DPNORM_ERR_ALIGN;
+  if (c) {
+    st = check_C(C);
+    if (st != DPNORM_OK) return st;
+  }
+  if (hc.bytes > 0 && !ws) return DPNORM_ERR_NULL;
+  if (ws_bytes < hc.bytes) return DPNORM_ERR_WORKSPACE;
+  if (ws && !aligned(ws, kAlign)) return DPNORM_ERR_ALIGN;
+  // outputs must not overlap any input or the workspace
+  const size_t nb = (size_t)B * 4;
+  const size_t e = esize(dt);
+  for (int64_t l = 0; l < L; ++l) {
+    const dpnorm_layer& y = layers[l];
+    const size_t sa = (size_t)B * T * y.d * e, sg = (size_t)B * T * y.p * e, sp = (size_t)y.p * k * e;
+    for (const float* o : {(const float*)n, (const float*)c}) {
+      if (!o) continue;
+      if (overlaps(o, nb, y.A, sa) || overlaps(o, nb, y.G, sg) || overlaps(o, nb, y.P, sp)) return DPNORM_ERR_VALUE;
+    }
+  }
+  if (overlaps(n, nb, ws, hc.bytes) || (c && overlaps(c, nb, ws, hc.bytes))) return DPNORM_ERR_VALUE;
+  if (c && c != n && overlaps(c, nb, n, nb)) return DPNORM_ERR_VALUE;
+  if (trace) {
+    if (!trace->events || !trace->kinds) return DPNORM_ERR_NULL;
+    const int need = pass_launches(hc.plan, (int)L) + 1;
+    if (trace->capacity < need + 1) return DPNORM_ERR_SIZE;
+  }
+
+  Tracer tr;
+  tr.t = trace;
+  tr.s = stream;
+  hipError_t he = tr.begin();
+  if (he == hipSuccess) he = run_pass(hc.plan, hc.layers, (char*)ws, stream, tr);
+  if (he == hipSuccess)
+    he = launch_finish((const double2*)((char*)ws + hc.plan.off_partials), (int32_t)B, hc.plan.slots, n, accumulate,
+                       nullptr, nullptr, c, c ? C : 1.f, c ? 1 : 0, stream);
+  if (he == hipSuccess) he = tr.mark(DPNORM_KERNEL_FINISH);
+  return hip_status(he);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int dpnorm_version(void) { return 100; }
+
+const char* dpnorm_status_string(int status) {
+  switch (status) {
+    case DPNORM_OK: return "DPNORM_OK";
+    case DPNORM_ERR_NULL: return "DPNORM_ERR_NULL: a required pointer is NULL";
+    case DPNORM_ERR_SIZE: return "DPNORM_ERR_SIZE: a size is out of range or misaligned";
+    case DPNORM_ERR_DTYPE: return "DPNORM_ERR_DTYPE: unknown element type or route";
+    case DPNORM_ERR_VALUE: return "DPNORM_ERR_VALUE: invalid value or overlapping output";
+    case DPNORM_ERR_WORKSPACE: return "DPNORM_ERR_WORKSPACE: workspace smaller than the query";
+    case DPNORM_ERR_ALIGN: return "DPNORM_ERR_ALIGN: pointer not aligned";
+    case DPNORM_ERR_HIP: return "DPNORM_ERR_HIP: a HIP launch or call failed";
+    default: return "unknown dpnorm status";
+  }
+}
+
+dpnorm_status dpnorm_hutchpp_split(int64_t k, int64_t* m_s, int64_t* m_t) {
+  if (!m_s || !m_t) return DPNORM_ERR_NULL;
+  if (k < 3 || k > 96) return DPNORM_ERR_SIZE;
+  *m_s = (k + 2) / 3;
+  *m_t = k - 2 * *m_s;
+  if (*m_t < 1) return DPNORM_ERR_SIZE;
+  return DPNORM_OK;
+}
+
+dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, int64_t k,
+                                     size_t* bytes) {
+  if (!bytes) return DPNORM_ERR_NULL;
+  dpnorm_layer y;
+  y.A = y.G = y.P = nullptr;
+  y.d = d;
+  y.p = p;
+  HutchCall hc;
+  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, hc);
+  if (st != DPNORM_OK) return st;
+  *bytes = hc.bytes;
+  return DPNORM_OK;
+}
+
+dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                             int64_t T, int64_t k, size_t* bytes) {
+  if (!bytes) return DPNORM_ERR_NULL;
+  HutchCall hc;
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, hc);
+  if (st != DPNORM_OK) return st;
+  *bytes = hc.bytes;
+  return DPNORM_OK;
+}
+
+dpnorm_status dpnorm_hutch(const void* A, const void* G, const void* P, dpnorm_dtype dt, int64_t B, int64_t T,
+                           int64_t d, int64_t p, int64_t k, float* n, int accumulate, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  dpnorm_layer y;
+  y.A = A;
+  y.G = G;
+  y.P = P;
+  y.d = d;
+  y.p = p;
+  return hutch_impl(&y, 1, dt, B, T, k, n, accumulate, nullptr, 1.f, ws, ws_bytes, stream, nullptr);
+}
+
+dpnorm_status dpnorm_hutch_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T,
+                                   int64_t k, float* n, int accumulate, float* c, float C, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, nullptr);
+}
+
+dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                          int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
+                                          void* ws, size_t ws_bytes, hipStream_t stream, dpnorm_trace* trace) {
+  if (!trace) return DPNORM_ERR_NULL;
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, trace);
+}
+
+dpnorm_status dpnorm_clip_factors(const float* n, int64_t B, float C, float* c, hipStream_t stream) {
+  if (!n || !c) return DPNORM_ERR_NULL;
+  if (B < 1 || B > ((int64_t)1 << 30)) return DPNORM_ERR_SIZE;
+  const dpnorm_status st = check_C(C);
+  if (st != DPNORM_OK) return st;
+  if (!aligned(n, 4) || !aligned(c, 4)) return DPNORM_ERR_ALIGN;
+  if (c != n && overlaps(c, (size_t)B * 4, n, (size_t)B * 4)) return DPNORM_ERR_VALUE;
+  return hip_status(launch_clip(n, (int32_t)B, C, c, stream));
+}
+
+dpnorm_status dpnorm_event_create(hipEvent_t* ev) {
+  if (!ev) return DPNORM_ERR_NULL;
+  return hip_status(hipEventCreate(ev));
+}
+dpnorm_status dpnorm_event_destroy(hipEvent_t ev) {
+  if (!ev) return DPNORM_ERR_NULL;
+  return hip_status(hipEventDestroy(ev));
+}
+dpnorm_status dpnorm_event_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms) {
+  if (!start || !stop || !ms) return DPNORM_ERR_NULL;
+  return hip_status(hipEventElapsedTime(ms, start, stop));
+}
+dpnorm_status dpnorm_event_record(hipEvent_t ev, hipStream_t stream) {
+  if (!ev) return DPNORM_ERR_NULL;
+  return hip_status(hipEventRecord(ev, stream));
+}
+dpnorm_status dpnorm_event_synchronize(hipEvent_t ev) {
+  if (!ev) return DPNORM_ERR_NULL;
+  return hip_status(hipEventSynchronize(ev));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+//
+// Every projected contraction in the library has the same two-stage shape:
+//   stage 1 (row projection):  V_i = X1_i W      X1_i [T][w1], W [w1][NC]
+//   stage 2 (T contraction):   Y_i = X2_i^T V_i  X2_i [T][w2], Y_i [w2][NC]
+// followed either by the squared Frobenius norm of Y_i (split into two column
+// groups, so Hutch++ gets its head and tail from one pass) or by storing Y_i.
+// For the Hutchinson estimate X1 = G, W = P, X2 = A. The host describes each
+// layer of a call once; a prepare kernel writes those descriptions, the work
+// item lists and the MFMA-packed W into the workspace, so one launch of each
+// stage covers every layer of a call.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpn {
+
+constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
+constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
+constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
+constexpr int kPrepChunk = 16;    // layers described per prepare launch (kernel-argument table)
+
+enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1 };
+
+// Device-side description of one layer (written by the prepare kernel).
+struct LayerRec {
+  const void* X1;      // [B][T][w1]
+  const void* W;       // packed W (see PrepLayer)
+  void* V;             // stage-1 output: bf16 hi/lo fragments or fp32 rows
+  const void* X2;      // [B][T][w2]
+  float* Ypart;        // split-T partial tiles [nsplit][B][w2][NC] (NULL if nsplit == 1 and no store)
+  float* Yout;         // stored Y [B][w2][NC] (store mode only)
+  int64_t w_stride_b;  // packed-W units between samples (0: W shared by the batch)
+  int32_t w1, w2;
+  int32_t slot_base;   // first partial slot of this layer within a sample
+  int32_t split;       // columns < split go to the first sum, the rest to the second
+};
+
+// Host-filled description used by the prepare kernel.
+struct PrepLayer {
+  LayerRec rec;
+  const void* wsrc;        // W source, row-major [rows][ld] (per sample: + smp * wsrc_stride_b)
+  int64_t wsrc_stride_b;   // source elements between samples (0: shared)
+  int32_t wsrc_type;       // SrcType
+  int32_t ld, ncols;       // source row stride and valid columns (< NC pads with zeros)
+  int32_t nsamples;        // 1 (shared W) or B
+  int32_t layer;           // index of this layer in the record table
+  int32_t unit_begin;      // first prepare unit of this layer within the launch
+  int32_t n_pack;          // packing units
+  int32_t k1_begin, n1;    // stage-1 items: global range and count
+  int32_t k2_begin, n2;    // stage-2 items: global range and count
+  int32_t ubs;             // stage-2 column blocks of X2 per sample
+  int32_t pad_;
+};
+
+struct PrepArgs {
+  PrepLayer L[kPrepChunk];
+  LayerRec* recs;
+  int4* items1;            // (layer, sample, row block, 0)
+  int4* items2;            // (layer, sample, column block, T split)
+  int32_t nlayers, total_units;
+  int32_t NCB, HL;         // packed W: column blocks of 16, hi/lo halves (bf16 target)
+  int32_t f32_target;      // pack W as fp32 rows [rows16][NC] instead of bf16 fragments
+  int32_t rbs;             // stage-1 row blocks per sample (Tpad / kRowsK1)
+  int32_t nsplit;          // stage-2 T splits
+};
+
+struct StageArgs {
+  const LayerRec* recs;
+  const int4* items;
+  int32_t n_items;
+  int32_t B, T, Tpad, nsplit;
+  int32_t slots_per_sample;
+  double2* partials;       // [B][slots] (sum of squares below / above split)
+};
+
+// mode for stage 2 and the split-T reduction
+enum Mode : int32_t { MODE_SQ = 0, MODE_STORE = 1 };
+
+hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStream_t s);
+// direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
+// itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s);
+hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s);
+hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, float* n, int accumulate,
+                         float* head, float* tail, float* c, float C, int with_clip, hipStream_t s);
+hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s);
+
+}  // namespace dpn

@@ -1,0 +1,580 @@
+// Kernels of the projected-contraction path on gfx950: the prepare pass
+// (layer records, work-item lists, MFMA-packed W), the skinny row projection
+// V = X1 W (stage 1), the T contraction Y = X2^T V with a fused squared
+// Frobenius reduction (stage 2), the split-T reduction, the per-sample
+// finisher and the clip factors.
+//
+// Method ('Efficient DP-SGD for LLMs with Randomized Clipping', papernotes.org
+// note, 关键设计 › Hutchinson 随机投影估范数): the squared per-sample gradient
+// norm of a linear layer is estimated by ||A_i^T (G_i P)||_F^2 with G P formed
+// first; 方法详解 › 整体框架: estimates are summed over the layers of a sample
+// and turned into the clip factor min(C / sqrt(n_i), 1).
+//
+// Both contractions are k wide (2k flops per element read, k = 32 on the
+// pages), far below the bf16 MFMA ridge, so the kernels are bound by streaming
+// X1 and X2 from HBM once each. The fp32 intermediate V is handed to the bf16
+// MFMA of stage 2 as a hi + lo pair of bf16 values (error <= 2^-17 relative).
+#include "device_common.h"
+#include "internal.h"
+
+namespace dpn {
+
+// ---------------------------------------------------------------------------
+// Prepare: one thread per unit. Units of a layer, in order: packed-W units,
+// stage-1 item entries, stage-2 item entries, and one unit for the record.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float load_src(const void* p, int64_t idx, int type) {
+  if (type == SRC_BF16) return bf16_bits_to_f32(((const uint16_t*)p)[idx]);
+  return ((const float*)p)[idx];
+}
+
+__global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
+  const int unit = blockIdx.x * 256 + threadIdx.x;
+  if (unit >= a.total_units) return;
+  int l = 0;
+  while (l + 1 < a.nlayers && unit >= a.L[l + 1].unit_begin) ++l;
+  const PrepLayer& P = a.L[l];
+  int r = unit - P.unit_begin;
+  const int NCB = a.NCB, NC = 16 * NCB;
+
+  if (r < P.n_pack) {
+    const int rows = P.rec.w1;
+    if (!a.f32_target) {
+      // bf16 fragments for the B operand of stage 1: unit (smp, ks, jb, h,
+      // lane) holds rows v = 32 ks + 8 (lane / 16) + s, s = 0..7, of column
+      // 16 jb + lane % 16; h = 0 is the bf16 value (hi), h = 1 the residual.
+      const int HL = a.HL;
+      const int nks = (rows + 31) / 32;
+      const int per_s = nks * NCB * HL * 64;
+      const int smp = r / per_s;
+      int q = r - smp * per_s;
+      const int lane = q & 63;
+      q >>= 6;
+      const int h = q % HL;
+      q /= HL;
+      const int jb = q % NCB;
+      const int ks = q / NCB;
+      const int c = 16 * jb + (lane & 15);
+      const int v0 = 32 * ks + 8 * (lane >> 4);
+      uint32_t b[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int v = v0 + s;
+        float x = 0.f;
+        if (v < rows && c < P.ncols)
+          x = load_src(P.wsrc, smp * P.wsrc_stride_b + (int64_t)v * P.ld + c, P.wsrc_type);
+        uint32_t hi, lo;
+        split_bf16(x, hi, lo);
+        b[s] = h ? lo : hi;
+      }
+      uint4* dst = (uint4*)P.rec.W + smp * P.rec.w_stride_b;
+      dst[(int64_t)((ks * NCB + jb) * HL + h) * 64 + lane] = pack8(b);
+    } else {
+      // fp32 rows [rows16][NC], zero padded.
+      const int rows16 = (rows + 15) / 16 * 16;
+      const int per_s = rows16 * NC;
+      const int smp = r / per_s;
+      const int q = r - smp * per_s;
+      const int v = q / NC, c = q - v * NC;
+      float x = 0.f;
+      if (v < rows && c < P.ncols)
+        x = load_src(P.wsrc, smp * P.wsrc_stride_b + (int64_t)v * P.ld + c, P.wsrc_type);
+      ((float*)P.rec.W)[smp * P.rec.w_stride_b + q] = x;
+    }
+    return;
+  }
+  r -= P.n_pack;
+  if (r < P.n1) {
+    const int i = r / a.rbs, rb = r - i * a.rbs;
+    a.items1[P.k1_begin + r] = make_int4(P.layer, i, rb, 0);
+    return;
+  }
+  r -= P.n1;
+  if (r < P.n2) {
+    // T split innermost: the split-T reduction finds item (i, ub) at a
+    // multiple of nsplit.
+    const int ts = r % a.nsplit, q = r / a.nsplit;
+    const int ub = q % P.ubs, i = q / P.ubs;
+    a.items2[P.k2_begin + r] = make_int4(P.layer, i, ub, ts);
+    return;
+  }
+  a.recs[P.layer] = P.rec;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1, bf16: V = X1 W for one sample. Each wave owns 32 rows (two 16-row
+// MFMA tiles) and walks the whole contraction in 32-wide K steps, four steps
+// per stage with the next stage's loads in flight. The result is written as
+// hi/lo bf16 B-operand fragments of stage 2: lane l already holds rows
+// slot_row(l / 16, s) of column l % 16, so no data leaves the lane.
+// V layout: [B][Tpad/32][NCB][2][64] uint4.
+// ---------------------------------------------------------------------------
+template <int NCB, int HL>
+__global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
+  constexpr int U = 4;
+  const int4 it = a.items[blockIdx.x];
+  const LayerRec* L = a.recs + it.x;
+  const int i = it.y, rb = it.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int w = L->w1, T = a.T;
+  const int r0 = rb * kRowsK1 + 32 * wv;
+  if (r0 >= T) return;  // chunk entirely past the sequence: stage 2 never reads it
+  const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
+  const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;
+  const int nks = (w + 31) >> 5;
+  const bool ok0 = r0 + n < T, ok1 = r0 + 16 + n < T;
+  const uint16_t* x0 = X + (int64_t)(r0 + n) * w + 8 * g;
+  const uint16_t* x1 = X + (int64_t)(r0 + 16 + n) * w + 8 * g;
+
+  f32x4_t acc[2][NCB];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) acc[mt][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  uint4 ga[U][2], wa[U][NCB][HL];
+  auto load = [&](int ks0, uint4 (&gg)[U][2], uint4 (&ww)[U][NCB][HL]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u;
+      const bool kok = ks < nks;
+      const bool vok = kok && (32 * ks + 8 * g < w);
+      gg[u][0] = (vok && ok0) ? *(const uint4*)(x0 + 32 * ks) : z;
+      gg[u][1] = (vok && ok1) ? *(const uint4*)(x1 + 32 * ks) : z;
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int h = 0; h < HL; ++h) ww[u][jb][h] = kok ? Wp[((ks * NCB + jb) * HL + h) * 64] : z;
+    }
+  };
+
+  load(0, ga, wa);
+  for (int ks0 = 0; ks0 < nks; ks0 += U) {
+    uint4 gb[U][2], wb[U][NCB][HL];
+    load(ks0 + U, gb, wb);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int h = 0; h < HL; ++h) {
+          acc[0][jb] = mfma_bf16(ga[u][0], wa[u][jb][h], acc[0][jb]);
+          acc[1][jb] = mfma_bf16(ga[u][1], wa[u][jb][h], acc[1][jb]);
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ga[u][0] = gb[u][0];
+      ga[u][1] = gb[u][1];
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int h = 0; h < HL; ++h) wa[u][jb][h] = wb[u][jb][h];
+    }
+  }
+
+  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32) * (NCB * 2 * 64) + lane;
+#pragma unroll
+  for (int jb = 0; jb < NCB; ++jb) {
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) split_bf16(acc[s >> 2][jb][s & 3], hi[s], lo[s]);
+    out[(jb * 2 + 0) * 64] = pack8(hi);
+    out[(jb * 2 + 1) * 64] = pack8(lo);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1, fp32: the same decomposition with v_mfma_f32_16x16x4f32. A lane
+// loads 4 consecutive columns of its row and feeds them to four MFMAs (K slot
+// l / 16 stands for column 16 ks + 4 (l / 16) + q of MFMA q).
+// V layout: [B][Tpad][NC] float.
+// ---------------------------------------------------------------------------
+template <int NCB>
+__global__ void __launch_bounds__(256) k_rowproj_f32(StageArgs a) {
+  constexpr int NC = 16 * NCB;
+  const int4 it = a.items[blockIdx.x];
+  const LayerRec* L = a.recs + it.x;
+  const int i = it.y, rb = it.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int w = L->w1, T = a.T;
+  const int r0 = rb * kRowsK1 + 32 * wv;
+  if (r0 >= T) return;
+  const float* X = (const float*)L->X1 + (int64_t)i * T * w;
+  const float* Wf = (const float*)L->W + i * L->w_stride_b;
+  const int nks = (w + 15) >> 4;
+  const bool ok0 = r0 + n < T, ok1 = r0 + 16 + n < T;
+  const float* x0 = X + (int64_t)(r0 + n) * w + 4 * g;
+  const float* x1 = X + (int64_t)(r0 + 16 + n) * w + 4 * g;
+
+  f32x4_t acc[2][NCB];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) acc[mt][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int ks = 0; ks < nks; ++ks) {
+    const int v = 16 * ks + 4 * g;
+    const bool vok = v < w;
+    const float4 g0 = (vok && ok0) ? *(const float4*)(x0 + 16 * ks) : z;
+    const float4 g1 = (vok && ok1) ? *(const float4*)(x1 + 16 * ks) : z;
+    const float gv0[4] = {g0.x, g0.y, g0.z, g0.w};
+    const float gv1[4] = {g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb) {
+        const float wq = Wf[(int64_t)(v + q) * NC + 16 * jb + n];
+        acc[0][jb] = mfma_f32(gv0[q], wq, acc[0][jb]);
+        acc[1][jb] = mfma_f32(gv1[q], wq, acc[1][jb]);
+      }
+  }
+
+  float* out = (float*)L->V + ((int64_t)i * a.Tpad + r0) * NC;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(16 * mt + 4 * g + r) * NC + 16 * jb + n] = acc[mt][jb][r];
+}
+
+// ---------------------------------------------------------------------------
+// Stage-2 epilogues.
+// direct: squared Frobenius sums of the tile, columns < split and the rest,
+//         reduced over the work group in a fixed order into one partial slot.
+// else:   the tile is stored to Ypart[ts][i][u][NC].
+// Lane l's accumulator (e, jb, r) is Y[u0 + ustride (4 (l/16) + r) + e][16 jb + l%16].
+// ---------------------------------------------------------------------------
+template <int NCB, int NE, bool DIRECT>
+__device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const LayerRec* L, f32x4_t (&acc)[NE][NCB],
+                                                   int i, int ub, int ts, int wave_u0, int ustride, int lane,
+                                                   int wv) {
+  constexpr int NC = 16 * NCB;
+  const int n = lane & 15, g = lane >> 4;
+  if (DIRECT) {
+    __shared__ double red[4][2];
+    const int split = L->split;
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double y = (double)acc[e][jb][r];
+          if (16 * jb + n < split) s0 += y * y;
+          else s1 += y * y;
+        }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      red[wv][0] = s0;
+      red[wv][1] = s1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub] =
+          make_double2((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]),
+                       (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]));
+  } else {
+    const int w = L->w2;
+    float* Y = L->Ypart + ((int64_t)ts * a.B + i) * w * NC;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int u = wave_u0 + ustride * (4 * g + r) + e;
+        if (u < w) {
+#pragma unroll
+          for (int jb = 0; jb < NCB; ++jb) Y[(int64_t)u * NC + 16 * jb + n] = acc[e][jb][r];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2, bf16: Y = X2^T V over the chunks of one T split, for 512 columns
+// of X2 (4 waves x 128). Per 32-row chunk a lane loads 8 rows (slot_row) of
+// its 8 consecutive columns, transposes the 8 x 8 block in registers so the
+// contraction index runs along the MFMA K slots, and multiplies it against
+// the hi and lo fragments of V; the next chunk's loads are in flight meanwhile.
+// ---------------------------------------------------------------------------
+template <int NCB, bool DIRECT>
+__global__ void __launch_bounds__(256, 2) k_tcontract_bf16(StageArgs a) {
+  const int4 it = a.items[xcd_item(blockIdx.x, (uint32_t)a.n_items)];
+  const LayerRec* L = a.recs + it.x;
+  const int i = it.y, ub = it.z, ts = it.w;
+  const int w = L->w2, T = a.T;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int wave_u0 = ub * kColsK2Bf16 + wv * 128;
+  const bool uok = wave_u0 + 8 * n < w;
+  const uint16_t* X = (const uint16_t*)L->X2 + (int64_t)i * T * w + wave_u0 + 8 * n;
+  const uint4* V = (const uint4*)L->V + (int64_t)i * (a.Tpad / 32) * (NCB * 2 * 64) + lane;
+  const int nch = (T + 31) >> 5;
+  const int c0 = (int)((int64_t)ts * nch / a.nsplit), c1 = (int)((int64_t)(ts + 1) * nch / a.nsplit);
+
+  f32x4_t acc[8][NCB];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  auto load = [&](int c, uint4 (&raw)[8], uint4 (&bv)[NCB][2]) {
+    const bool cok = c < c1;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int t = 32 * c + slot_row(g, s);
+      raw[s] = (cok && uok && t < T) ? *(const uint4*)(X + (int64_t)t * w) : z;
+    }
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bv[jb][h] = cok ? V[((int64_t)(c * NCB + jb) * 2 + h) * 64] : z;
+  };
+
+  if (wave_u0 < w) {
+    uint4 raw[8], bv[NCB][2];
+    load(c0, raw, bv);
+    for (int c = c0; c < c1; ++c) {
+      uint4 rawn[8], bvn[NCB][2];
+      load(c + 1, rawn, bvn);
+      uint4 op[8];
+      transpose8x8_bf16(raw, op);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb) {
+          acc[e][jb] = mfma_bf16(op[e], bv[jb][0], acc[e][jb]);
+          acc[e][jb] = mfma_bf16(op[e], bv[jb][1], acc[e][jb]);
+        }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = rawn[s];
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb) {
+        bv[jb][0] = bvn[jb][0];
+        bv[jb][1] = bvn[jb][1];
+      }
+    }
+  }
+  tcontract_epilogue<NCB, 8, DIRECT>(a, L, acc, i, ub, ts, wave_u0, 8, lane, wv);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2, fp32: 4 rows per MFMA step; a lane's float4 of 4 consecutive
+// columns feeds four MFMAs (one per column offset e), so no transpose is
+// needed. 256 columns per work group (4 waves x 64).
+// ---------------------------------------------------------------------------
+template <int NCB, bool DIRECT>
+__global__ void __launch_bounds__(256) k_tcontract_f32(StageArgs a) {
+  constexpr int NC = 16 * NCB;
+  const int4 it = a.items[xcd_item(blockIdx.x, (uint32_t)a.n_items)];
+  const LayerRec* L = a.recs + it.x;
+  const int i = it.y, ub = it.z, ts = it.w;
+  const int w = L->w2, T = a.T;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int wave_u0 = ub * kColsK2F32 + wv * 64;
+  const bool uok = wave_u0 + 4 * n < w;
+  const float* X = (const float*)L->X2 + (int64_t)i * T * w + wave_u0 + 4 * n;
+  const float* V = (const float*)L->V + (int64_t)i * a.Tpad * NC + n;
+  const int nch = (T + 31) >> 5;
+  const int c0 = (int)((int64_t)ts * nch / a.nsplit), c1 = (int)((int64_t)(ts + 1) * nch / a.nsplit);
+  const int t_end = min(T, 32 * c1);
+
+  f32x4_t acc[4][NCB];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (wave_u0 < w) {
+    for (int t0 = 32 * c0; t0 < t_end; t0 += 4) {
+      const int t = t0 + g;
+      const float4 x = (uok && t < T) ? *(const float4*)(X + (int64_t)t * w) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb) {
+        const float b = (t < T) ? V[(int64_t)t * NC + 16 * jb] : 0.f;
+        acc[0][jb] = mfma_f32(x.x, b, acc[0][jb]);
+        acc[1][jb] = mfma_f32(x.y, b, acc[1][jb]);
+        acc[2][jb] = mfma_f32(x.z, b, acc[2][jb]);
+        acc[3][jb] = mfma_f32(x.w, b, acc[3][jb]);
+      }
+    }
+  }
+  tcontract_epilogue<NCB, 4, DIRECT>(a, L, acc, i, ub, ts, wave_u0, 4, lane, wv);
+}
+
+// ---------------------------------------------------------------------------
+// Split-T reduction: for one (layer, sample, column block) sum the nsplit
+// partial tiles in split order (fp64), then either square and reduce into the
+// partial slot (MODE_SQ) or store Y (MODE_STORE).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_block) {
+  const int4 it = a.items[(int64_t)blockIdx.x * a.nsplit];
+  const LayerRec* L = a.recs + it.x;
+  const int i = it.y, ub = it.z;
+  const int w = L->w2;
+  const int u0 = ub * cols_per_block;
+  const int ucount = min(cols_per_block, w - u0);
+  const int nel = ucount * NC;
+  const int64_t tile = (int64_t)a.B * w * NC;
+  const float* Yp = L->Ypart + ((int64_t)i * w + u0) * NC;
+  double s0 = 0.0, s1 = 0.0;
+  const int split = L->split;
+  for (int e = threadIdx.x; e < nel; e += 256) {
+    double y = 0.0;
+    for (int ts = 0; ts < a.nsplit; ++ts) y += (double)Yp[ts * tile + e];
+    if (MODE == MODE_SQ) {
+      if (e % NC < split) s0 += y * y;
+      else s1 += y * y;
+    } else {
+      L->Yout[((int64_t)i * w + u0) * NC + e] = (float)y;
+    }
+  }
+  if (MODE == MODE_SQ) {
+    __shared__ double red[4][2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      red[wv][0] = s0;
+      red[wv][1] = s1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub] =
+          make_double2((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]),
+                       (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finisher: per sample, sum the partial slots in a fixed order (strided per
+// thread, then a fixed tree), add to n when accumulating, and optionally emit
+// the two column-group sums (head / tail) and the clip factor.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float clip_value(float n, float C) {
+  if (n != n) return n;
+  if (!(n > 0.f)) return 1.f;
+  const double c = (double)C / sqrt((double)n);
+  return (float)(c < 1.0 ? c : 1.0);
+}
+
+__global__ void __launch_bounds__(256) k_finish(const double2* __restrict__ partials, int32_t slots, float* n,
+                                                int accumulate, float* head, float* tail, float* c, float C,
+                                                int with_clip) {
+  __shared__ double r0[256], r1[256];
+  const int i = blockIdx.x, t = threadIdx.x;
+  const double2* P = partials + (int64_t)i * slots;
+  double s0 = 0.0, s1 = 0.0;
+  for (int j = t; j < slots; j += 256) {
+    const double2 v = P[j];
+    s0 += v.x;
+    s1 += v.y;
+  }
+  r0[t] = s0;
+  r1[t] = s1;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) {
+      r0[t] += r0[t + h];
+      r1[t] += r1[t + h];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double tot = r0[0] + r1[0];
+    const float nv = (float)(accumulate ? (double)n[i] + tot : tot);
+    n[i] = nv;
+    if (head) head[i] = (float)r0[0];
+    if (tail) tail[i] = (float)r1[0];
+    if (with_clip) c[i] = clip_value(nv, C);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_clip(const float* n, int32_t B, float C, float* c) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < B) c[i] = clip_value(n[i], C);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
+  if (a.total_units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prepare, dim3((a.total_units + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStream_t s) {
+  if (a.n_items <= 0) return hipSuccess;
+  const dim3 grid(a.n_items), blk(256);
+  if (bf16) {
+    if (HL == 1) {
+      if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1>), grid, blk, 0, s, a);
+      else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_rowproj_bf16<4, 1>), grid, blk, 0, s, a);
+    } else {
+      if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2>), grid, blk, 0, s, a);
+      else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_rowproj_bf16<4, 2>), grid, blk, 0, s, a);
+    }
+  } else {
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_f32<1>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_f32<2>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_f32<4>), grid, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s) {
+  if (a.n_items <= 0) return hipSuccess;
+  const dim3 grid(a.n_items), blk(256);
+#define DPN_TC(KER, N)                                                          \
+  do {                                                                          \
+    if (direct) hipLaunchKernelGGL((KER<N, true>), grid, blk, 0, s, a);         \
+    else hipLaunchKernelGGL((KER<N, false>), grid, blk, 0, s, a);               \
+  } while (0)
+  if (bf16) {
+    if (NCB == 1) DPN_TC(k_tcontract_bf16, 1);
+    else if (NCB == 2) DPN_TC(k_tcontract_bf16, 2);
+    else DPN_TC(k_tcontract_bf16, 4);
+  } else {
+    if (NCB == 1) DPN_TC(k_tcontract_f32, 1);
+    else if (NCB == 2) DPN_TC(k_tcontract_f32, 2);
+    else DPN_TC(k_tcontract_f32, 4);
+  }
+#undef DPN_TC
+  return hipGetLastError();
+}
+
+hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s) {
+  const int blocks = a.n_items / a.nsplit;
+  if (blocks <= 0) return hipSuccess;
+  if (mode == MODE_SQ)
+    hipLaunchKernelGGL(k_ysum<MODE_SQ>, dim3(blocks), dim3(256), 0, s, a, 16 * NCB, cols_per_block);
+  else
+    hipLaunchKernelGGL(k_ysum<MODE_STORE>, dim3(blocks), dim3(256), 0, s, a, 16 * NCB, cols_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, float* n, int accumulate, float* head,
+                         float* tail, float* c, float C, int with_clip, hipStream_t s) {
+  hipLaunchKernelGGL(k_finish, dim3(B), dim3(256), 0, s, partials, slots, n, accumulate, head, tail, c, C,
+                     with_clip);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s) {
+  hipLaunchKernelGGL(k_clip, dim3((B + 255) / 256), dim3(256), 0, s, n, B, C, c);
+  return hipGetLastError();
+}
+
+}  // namespace dpn

@@ -1,0 +1,195 @@
+"""GPU parity of the Hutchinson path against the fp64 CPU oracle.
+
+Same seeded inputs and the same P on both sides; per-sample relative error
+|gpu - oracle| / |oracle| must stay within 1e-3 for bf16 inputs (fp32
+accumulation) and 1e-5 for fp32 inputs, for the estimates and the clip
+factors. Shapes span several work items with ragged tails in T, d, p and k.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 1e-3, torch.float32: 1e-5}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def rel_err(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    out = np.empty_like(want)
+    for j, (g, w) in enumerate(zip(got, want)):
+        out[j] = abs(g) / 1e-30 if w == 0 else abs(g - w) / abs(w)
+    return out
+
+
+def check(got, want, tol, what):
+    err = rel_err(got, want)
+    print(f"{what}: max rel err {err.max():.3e}", flush=True)
+    assert np.all(err <= tol), f"{what}: rel err {err} > {tol}"
+
+
+def test_config1_fp32_hutch_and_clip():
+    import sample_grad_norms_amd as dp
+    prob = workloads.config1(device=dev())
+    n, c = dp.hutch_grouped([(prob.A, prob.G, prob.P)], C_clip=1.0)
+    n1 = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    want = oracle.hutch(prob.A, prob.G, prob.P)
+    check(n.cpu(), want, 1e-5, "config1 hutch grouped")
+    check(n1.cpu(), want, 1e-5, "config1 hutch")
+    check(c.cpu(), oracle.clip_factors(want, 1.0), 1e-5, "config1 clip")
+
+
+SHAPES_BF16 = [
+    # B, T, d, p, k
+    (3, 333, 1032, 520, 32),     # ragged T (not a multiple of 32 or 128), d past one column block, p % 32 != 0
+    (2, 95, 8, 8, 1),            # narrowest widths, k = 1
+    (1, 1, 512, 512, 32),        # a single token
+    (2, 4097, 256, 1024, 20),    # T one past a tile, k padded to 32 columns
+    (4, 200, 136, 64, 64),       # k = 64 (four column blocks)
+    (2, 128, 2048, 512, 16),     # one 16-column block
+    (1, 2500, 4096, 8192, 32),   # long rows on both sides, split T
+]
+
+
+@pytest.mark.parametrize("B,T,d,p,k", SHAPES_BF16)
+def test_hutch_bf16_shapes(B, T, d, p, k):
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(B, T, d, p, k, seed=B * 7 + T, device=dev(), dtype=torch.bfloat16)
+    n = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    check(n.cpu(), oracle.hutch(prob.A, prob.G, prob.P), 1e-3, f"bf16 B{B} T{T} d{d} p{p} k{k}")
+
+
+SHAPES_F32 = [
+    (2, 150, 260, 132, 8),
+    (1, 33, 4, 4, 3),
+    (3, 700, 1028, 36, 32),
+    (2, 64, 64, 2052, 64),
+]
+
+
+@pytest.mark.parametrize("B,T,d,p,k", SHAPES_F32)
+def test_hutch_f32_shapes(B, T, d, p, k):
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(B, T, d, p, k, seed=B * 5 + T, device=dev(), dtype=torch.float32)
+    n = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    check(n.cpu(), oracle.hutch(prob.A, prob.G, prob.P), 1e-5, f"f32 B{B} T{T} d{d} p{p} k{k}")
+
+
+def test_zero_inputs_give_zero_and_unit_clip():
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(2, 70, 64, 64, 8, seed=3, device=dev(), dtype=torch.bfloat16)
+    prob.G[1].zero_()
+    n, c = dp.hutch_grouped([(prob.A, prob.G, prob.P)], C_clip=1.0)
+    torch.cuda.synchronize()
+    assert n[1].item() == 0.0 and c[1].item() == 1.0
+    assert n[0].item() > 0.0
+
+
+def test_grouped_is_layer_sum_and_accumulates():
+    import sample_grad_norms_amd as dp
+    shapes = [(256, 64), (64, 512), (520, 136), (1024, 1024)]
+    B, T, k = 3, 257, 32
+    layers = []
+    for j, (d, p) in enumerate(shapes):
+        pr = workloads.random_problem(B, T, d, p, k, seed=100 + j, device=dev(), dtype=torch.bfloat16)
+        layers.append((pr.A, pr.G, pr.P))
+    n, c = dp.hutch_grouped(layers, C_clip=50.0)
+    acc = torch.zeros(B, dtype=torch.float32, device=dev())
+    for (A, G, P) in layers:
+        dp.hutch(A, G, P, out=acc, accumulate=True)
+    base = torch.full((B,), 5.0, dtype=torch.float32, device=dev())
+    dp.hutch_grouped(layers, out=base, accumulate=True)
+    torch.cuda.synchronize()
+    want = oracle.layer_sum([oracle.hutch(A, G, P) for (A, G, P) in layers])
+    check(n.cpu(), want, 1e-3, "grouped layer sum")
+    check(acc.cpu(), want, 1e-3, "accumulated single calls")
+    check(base.cpu(), want + 5.0, 1e-3, "grouped accumulate")
+    check(c.cpu(), oracle.clip_factors(want, 50.0), 1e-3, "grouped clip")
+
+
+def test_deterministic_bitwise():
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(2, 1500, 1024, 2048, 32, seed=9, device=dev(), dtype=torch.bfloat16)
+    a = dp.hutch(prob.A, prob.G, prob.P)
+    b = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_clip_factor_kernel_special_values():
+    import sample_grad_norms_amd as dp
+    n = torch.tensor([0.0, float("inf"), float("nan"), 4.0, 16.0, 1.0, 64.0, 1e-30], device=dev())
+    c = dp.clip_factors(n, 2.0)
+    torch.cuda.synchronize()
+    got = c.cpu().double().numpy()
+    want = oracle.clip_factors(n.cpu().double().numpy(), 2.0)
+    assert math.isnan(got[2]) and math.isnan(want[2])
+    keep = [0, 1, 3, 4, 5, 6, 7]
+    check(got[keep], want[keep], 1e-6, "clip special values")
+    # in place
+    m = n.clone()
+    dp.clip_factors(m, 2.0, out=m)
+    torch.cuda.synchronize()
+    assert torch.equal(m[keep].cpu(), c[keep].cpu())
+
+
+def test_config2_full_size():
+    import sample_grad_norms_amd as dp
+    for rescaled in (False, True):
+        prob = workloads.config2(device=dev(), rescaled=rescaled)
+        n, c = dp.hutch_grouped([(prob.A, prob.G, prob.P)], C_clip=1.0)
+        torch.cuda.synchronize()
+        want = oracle.hutch(prob.A, prob.G, prob.P)
+        wc = oracle.clip_factors(want, 1.0)
+        check(n.cpu(), want, 1e-3, prob.name)
+        check(c.cpu(), wc, 1e-3, prob.name + " clip")
+        if rescaled:
+            # the rescaled sub-case puts samples on both sides of C = 1
+            assert np.any(wc < 1.0) and np.any(wc == 1.0)
+
+
+def test_config3_full_size_stack():
+    """Llama-3.2-1B-shaped stack (16 x 7 projections, B=4, T=4096, k=32): the
+    grouped call as timed by the benchmark, against the oracle's layer sum.
+    The oracle runs on every projection of the first decoder layer and on
+    one projection of each kind in the last; the grouped call over all 112
+    projections must equal the per-projection single calls summed."""
+    import sample_grad_norms_amd as dp
+    projs = [workloads.config3_projection(j, device=dev()) for j in range(112)]
+    layers = [(q.A, q.G, q.P) for q in projs]
+    n_all, c_all = dp.hutch_grouped(layers, C_clip=1.0)
+    singles = []
+    for (A, G, P) in layers:
+        singles.append(dp.hutch(A, G, P))
+    torch.cuda.synchronize()
+    tot = torch.stack(singles).double().sum(0).cpu().numpy()
+    check(n_all.cpu(), tot, 1e-4, "config3 grouped vs sum of single calls")
+    subset = list(range(7)) + list(range(105, 112))
+    n_sub = dp.hutch_grouped([layers[j] for j in subset])
+    torch.cuda.synchronize()
+    want = oracle.layer_sum([oracle.hutch(*layers[j]) for j in subset])
+    check(n_sub.cpu(), want, 1e-3, "config3 first + last decoder layer vs oracle")
+    for j in subset:
+        check(singles[j].cpu(), oracle.hutch(*layers[j]), 1e-3, projs[j].name)
+    check(c_all.cpu(), oracle.clip_factors(n_all.cpu().double().numpy(), 1.0), 1e-5, "config3 clip")
+
+
+def test_config5_full_size_hutch():
+    import sample_grad_norms_amd as dp
+    prob = workloads.config5(device=dev())
+    n = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    check(n.cpu(), oracle.hutch(prob.A, prob.G, prob.P), 1e-3, prob.name)
