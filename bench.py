@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=4, help="decoder layers in the oracle's sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -86,6 +88,12 @@ def main():
     bytes_G = sum(G.numel() * G.element_size() for (_, G, _) in layers)
     bytes_P = sum(P.numel() * P.element_size() for (_, _, P) in layers)
     alg_bytes = bytes_A + bytes_G + bytes_P
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     def step(timer=None):

@@ -46,6 +46,28 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Global-memory accesses through the global address space. Pointers that a
+// kernel reads from a device-side record are generic to the compiler, which
+// would emit flat instructions; flat loads may alias LDS, so the compiler
+// would then wait for every outstanding direct-to-LDS load before each one.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+#define DPN_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  const u32x4_t v = *(const DPN_GLOBAL u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {  // non-temporal: streamed past the caches
+  const u32x4_t v = __builtin_nontemporal_load((const DPN_GLOBAL u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ldg_f32(const void* p) { return *(const DPN_GLOBAL float*)p; }
+__device__ __forceinline__ float4 ldg_f32x4(const void* p) {
+  const f32x4_t v = *(const DPN_GLOBAL f32x4_t*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stg16(void* p, const uint4& v) { *(DPN_GLOBAL u32x4_t*)p = u32x4_t{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ void stg_f32(void* p, float v) { *(DPN_GLOBAL float*)p = v; }
+
 __device__ __forceinline__ uint4 pack8(const uint32_t b[8]) {
   return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
 }

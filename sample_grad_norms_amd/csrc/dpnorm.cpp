@@ -73,7 +73,7 @@ struct PassPlan {
 int ncb_of(int64_t ncols) { return ncols <= 16 ? 1 : (ncols <= 32 ? 2 : 4); }
 
 size_t packed_units(const PassPlan& pl, int64_t rows) {
-  if (pl.bf16) return (size_t)((rows + 31) / 32) * pl.NCB * pl.HL * 64;  // uint4 units
+  if (pl.bf16) return (size_t)((rows + 63) / 64 * 2) * pl.NCB * pl.HL * 64;  // uint4 units, even K steps
   return (size_t)((rows + 15) / 16 * 16) * 16 * pl.NCB;                   // floats
 }
 

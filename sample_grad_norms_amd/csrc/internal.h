@@ -18,7 +18,7 @@ namespace dpn {
 constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
-constexpr int kPrepChunk = 16;    // layers described per prepare launch (kernel-argument table)
+constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
 
 enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1 };
 

@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
       // lane) holds rows v = 32 ks + 8 (lane / 16) + s, s = 0..7, of column
       // 16 jb + lane % 16; h = 0 is the bf16 value (hi), h = 1 the residual.
       const int HL = a.HL;
-      const int nks = (rows + 31) / 32;
+      const int nks = (rows + 63) / 64 * 2;  // even number of K steps: stage 1 loads two per stage
       const int per_s = nks * NCB * HL * 64;
       const int smp = r / per_s;
       int q = r - smp * per_s;
@@ -102,30 +102,89 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1, bf16: V = X1 W for one sample. Each wave owns 32 rows (two 16-row
-// MFMA tiles) and walks the whole contraction in 32-wide K steps, four steps
-// per stage with the next stage's loads in flight. The result is written as
-// hi/lo bf16 B-operand fragments of stage 2: lane l already holds rows
-// slot_row(l / 16, s) of column l % 16, so no data leaves the lane.
+// Stage 1, bf16: V = X1 W for 128 rows of one sample.
+//
+// X1 and the packed W are streamed into LDS 64 columns (one 128-byte line per
+// row) and two K steps at a time with direct global-to-LDS loads: every wave
+// instruction moves 1 KB of whole lines without using registers (X1 with
+// non-temporal loads, so the stream does not evict W from L2), and three
+// stages are in flight while one is multiplied. The loads are issued from
+// inline assembly so that the only waits on them are the ones placed here:
+// before each barrier a wave waits for its own loads of the stage about to be
+// read, and the later stages stay in flight.
+// Wave w owns rows 32w..32w+31 (two 16-row MFMA tiles); the 16-byte units of
+// an X1 row are XOR-swizzled by the row index so the A-operand reads spread
+// over the LDS banks. After the last stage lane l of wave w holds rows
+// slot_row(l / 16, s) of chunk w, so the hi/lo bf16 B-operand fragments of
+// stage 2 are written straight from the accumulators.
 // V layout: [B][Tpad/32][NCB][2][64] uint4.
 // ---------------------------------------------------------------------------
+constexpr int kK1Cols = 64;                          // columns of X1 per stage (one 128-byte line)
+constexpr int kK1XBytes = kRowsK1 * kK1Cols * 2;     // X1 bytes per stage (16 KB)
+constexpr int kK1XDma = kK1XBytes / 1024 / 4;        // 1 KB X1 instructions per wave per stage
+constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
+
+// s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt at max).
+#define DPN_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
+
+// 16 bytes per lane from global memory to LDS at lds_addr + 16 * lane
+// (lds_addr wave-uniform). M0 carries the LDS address; nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16_stream(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+// Work-group barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int NCB, int HL>
 __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
-  constexpr int U = 4;
+  constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per stage
+  constexpr int kStage = kK1XBytes + kWBlocks * 1024;
+  constexpr int kPerWave = kK1XDma + kWBlocks / 4;       // loads every wave issues per stage (at least)
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kK1Bufs * kStage];
   const int4 it = a.items[blockIdx.x];
   const LayerRec* L = a.recs + it.x;
   const int i = it.y, rb = it.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int w = L->w1, T = a.T;
-  const int r0 = rb * kRowsK1 + 32 * wv;
-  if (r0 >= T) return;  // chunk entirely past the sequence: stage 2 never reads it
+  const int r0 = rb * kRowsK1;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
-  const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;
-  const int nks = (w + 31) >> 5;
-  const bool ok0 = r0 + n < T, ok1 = r0 + 16 + n < T;
-  const uint16_t* x0 = X + (int64_t)(r0 + n) * w + 8 * g;
-  const uint16_t* x1 = X + (int64_t)(r0 + 16 + n) * w + 8 * g;
+  const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
+  const int nst = (w + kK1Cols - 1) / kK1Cols;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+
+  // X1 source of this lane: instruction j of wave wv fills LDS rows
+  // 8 (4 wv + j) + lane / 8 at unit position lane % 8, which holds global
+  // unit (lane % 8) ^ (row % 8). Rows past T and columns past w read the last
+  // valid row / unit instead: those values only ever meet zero rows of A or
+  // zero rows of W, so they contribute nothing.
+  const int urow0 = 32 * wv + (lane >> 3);
+  const int gunit = (lane & 7) ^ (urow0 & 7);  // row % 8 is the same for all j (rows step by 8)
+  auto dma = [&](int st) {
+    if (st >= nst) return;
+    const uint32_t buf = lds_base + (uint32_t)((st % kK1Bufs) * kStage);
+    int col = st * kK1Cols + gunit * 8;
+    col = col < w ? col : w - 8;
+#pragma unroll
+    for (int j = 0; j < kK1XDma; ++j) {
+      int row = r0 + urow0 + 8 * j;
+      row = row < T ? row : T - 1;
+      dma16_stream(X + (int64_t)row * w + col, buf + (uint32_t)((wv * kK1XDma + j) * 1024));
+    }
+#pragma unroll
+    for (int m0 = 0; m0 < (kWBlocks + 3) / 4; ++m0) {
+      const int m = 4 * m0 + wv;
+      if (m < kWBlocks) dma16(Wp + ((int64_t)st * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
+    }
+  };
 
   f32x4_t acc[2][NCB];
 #pragma unroll
@@ -133,55 +192,48 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int jb = 0; jb < NCB; ++jb) acc[mt][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  uint4 ga[U][2], wa[U][NCB][HL];
-  auto load = [&](int ks0, uint4 (&gg)[U][2], uint4 (&ww)[U][NCB][HL]) {
+  dma(0);
+  dma(1);
+  dma(2);
+  for (int st = 0; st < nst; ++st) {
+    // this wave's loads of stage st have landed once at most the later
+    // stages' loads are outstanding; the barrier then publishes every wave's
+    // loads of stage st and frees the buffer of stage st - 1
+    if (st + 2 < nst) DPN_WAIT_VMCNT(2 * kPerWave);
+    else if (st + 1 < nst) DPN_WAIT_VMCNT(kPerWave);
+    else DPN_WAIT_VMCNT(0);
+    block_barrier();
+    dma(st + 3);
+    const unsigned char* buf = lds + (st % kK1Bufs) * kStage;
+    const uint4* wf = (const uint4*)(buf + kK1XBytes) + lane;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = ks0 + u;
-      const bool kok = ks < nks;
-      const bool vok = kok && (32 * ks + 8 * g < w);
-      gg[u][0] = (vok && ok0) ? *(const uint4*)(x0 + 32 * ks) : z;
-      gg[u][1] = (vok && ok1) ? *(const uint4*)(x1 + 32 * ks) : z;
-#pragma unroll
-      for (int jb = 0; jb < NCB; ++jb)
-#pragma unroll
-        for (int h = 0; h < HL; ++h) ww[u][jb][h] = kok ? Wp[((ks * NCB + jb) * HL + h) * 64] : z;
-    }
-  };
-
-  load(0, ga, wa);
-  for (int ks0 = 0; ks0 < nks; ks0 += U) {
-    uint4 gb[U][2], wb[U][NCB][HL];
-    load(ks0 + U, gb, wb);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 f[NCB][HL];
 #pragma unroll
       for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-        for (int h = 0; h < HL; ++h) {
-          acc[0][jb] = mfma_bf16(ga[u][0], wa[u][jb][h], acc[0][jb]);
-          acc[1][jb] = mfma_bf16(ga[u][1], wa[u][jb][h], acc[1][jb]);
-        }
+        for (int h = 0; h < HL; ++h) f[jb][h] = wf[((kk * NCB + jb) * HL + h) * 64];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ga[u][0] = gb[u][0];
-      ga[u][1] = gb[u][1];
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = 32 * wv + 16 * mt + n;
+        const uint4 x = *(const uint4*)(buf + row * 128 + (((4 * kk + g) ^ (row & 7)) * 16));
 #pragma unroll
-      for (int jb = 0; jb < NCB; ++jb)
+        for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-        for (int h = 0; h < HL; ++h) wa[u][jb][h] = wb[u][jb][h];
+          for (int h = 0; h < HL; ++h) acc[mt][jb] = mfma_bf16(x, f[jb][h], acc[mt][jb]);
+      }
     }
   }
 
-  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32) * (NCB * 2 * 64) + lane;
+  if (r0 + 32 * wv >= T) return;  // chunk past the sequence: stage 2 never reads it
+  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32 + wv) * (NCB * 2 * 64) + lane;
 #pragma unroll
   for (int jb = 0; jb < NCB; ++jb) {
     uint32_t hi[8], lo[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) split_bf16(acc[s >> 2][jb][s & 3], hi[s], lo[s]);
-    out[(jb * 2 + 0) * 64] = pack8(hi);
-    out[(jb * 2 + 1) * 64] = pack8(lo);
+    stg16(out + (jb * 2 + 0) * 64, pack8(hi));
+    stg16(out + (jb * 2 + 1) * 64, pack8(lo));
   }
 }
 
@@ -290,7 +342,7 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
         const int u = wave_u0 + ustride * (4 * g + r) + e;
         if (u < w) {
 #pragma unroll
-          for (int jb = 0; jb < NCB; ++jb) Y[(int64_t)u * NC + 16 * jb + n] = acc[e][jb][r];
+          for (int jb = 0; jb < NCB; ++jb) stg_f32(Y + (int64_t)u * NC + 16 * jb + n, acc[e][jb][r]);
         }
       }
   }
@@ -330,12 +382,12 @@ __global__ void __launch_bounds__(256, 2) k_tcontract_bf16(StageArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int t = 32 * c + slot_row(g, s);
-      raw[s] = (cok && uok && t < T) ? *(const uint4*)(X + (int64_t)t * w) : z;
+      raw[s] = (cok && uok && t < T) ? ldg16_stream(X + (int64_t)t * w) : z;
     }
 #pragma unroll
     for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bv[jb][h] = cok ? V[((int64_t)(c * NCB + jb) * 2 + h) * 64] : z;
+      for (int h = 0; h < 2; ++h) bv[jb][h] = cok ? ldg16(V + ((int64_t)(c * NCB + jb) * 2 + h) * 64) : z;
   };
 
   if (wave_u0 < w) {
@@ -396,10 +448,10 @@ __global__ void __launch_bounds__(256) k_tcontract_f32(StageArgs a) {
   if (wave_u0 < w) {
     for (int t0 = 32 * c0; t0 < t_end; t0 += 4) {
       const int t = t0 + g;
-      const float4 x = (uok && t < T) ? *(const float4*)(X + (int64_t)t * w) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x = (uok && t < T) ? ldg_f32x4(X + (int64_t)t * w) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int jb = 0; jb < NCB; ++jb) {
-        const float b = (t < T) ? V[(int64_t)t * NC + 16 * jb] : 0.f;
+        const float b = (t < T) ? ldg_f32(V + (int64_t)t * NC + 16 * jb) : 0.f;
         acc[0][jb] = mfma_f32(x.x, b, acc[0][jb]);
         acc[1][jb] = mfma_f32(x.y, b, acc[1][jb]);
         acc[2][jb] = mfma_f32(x.z, b, acc[2][jb]);
