@@ -121,6 +121,11 @@ dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int6
                                      int64_t k, size_t* bytes);
 dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
                                              int64_t B, int64_t T, int64_t k, size_t* bytes);
+dpnorm_status dpnorm_hutchpp_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p,
+                                       int64_t k, size_t* bytes);
+dpnorm_status dpnorm_exact_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p,
+                                     dpnorm_route route, size_t* bytes);
+
 /* Hutchinson estimate of one layer (note: 关键设计 › Hutchinson; summary:
  * Kernmechanisme item 1): n_hat_i = ||A_i^T (G_i P)||_F^2 for every sample,
  * P [p][k] shared by the samples (caller draws N(0, 1/k) entries;
@@ -146,6 +151,37 @@ dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L,
                                           int64_t B, int64_t T, int64_t k, float* n, int accumulate,
                                           float* c, float C, void* ws, size_t ws_bytes,
                                           hipStream_t stream, dpnorm_trace* trace);
+
+/* Hutch++ estimate of one layer with budget k (note: 关键设计 › Hutch++;
+ * summary: Kernmechanisme item 2). With (m_s, m_t) from
+ * dpnorm_hutchpp_split(k), S is [p][m_s] (sketch, any scale; N(0,1)
+ * suggested) and P is [p][m_t] (tail, entries of variance 1/m_t), both shared
+ * by the samples. Per sample:
+ *   X = O S with O = G^T A A^T G, formed as G^T (A (A^T (G S)));
+ *   Q = orthonormal basis of Col(X) by Gram-Schmidt in fp64, each column
+ *       projected against the kept columns twice; column j of X is kept
+ *       when its residual exceeds 1e-5 times the largest column norm of X
+ *       (rank r_i <= m_s);
+ *   head = ||A^T (G Q)||_F^2, tail = ||A^T (G (P - Q Q^T P))||_F^2,
+ *   n_hat = head + tail.
+ * n (+)= n_hat as for dpnorm_hutch. head, tail (float [B]) and rank (int32
+ * [B]) are optional outputs (NULL to skip); they hold this call's values.
+ * k is the total budget, 3 <= k <= 96 (so m_s <= 32 and m_s + m_t <= 64). */
+dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const void* P, dpnorm_dtype dt,
+                             int64_t B, int64_t T, int64_t d, int64_t p, int64_t k, float* n,
+                             int accumulate, float* head, float* tail, int32_t* rank, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Exact squared per-sample norm n_i = ||A_i^T G_i||_F^2 (the comparator:
+ * note 研究背景与动机 and 相关工作, explicit gradients vs ghost clipping;
+ * summary: Complexiteitsreductie). DPNORM_EXACT_EXPLICIT sums squares of
+ * A^T G tiles (2 T d p flops per sample); DPNORM_EXACT_GRAM sums the product
+ * of A A^T and G G^T tiles (about 2 T^2 (d + p) flops with symmetry); AUTO
+ * picks explicit when d*p <= T*T. Nothing of size d x p or T x T is stored.
+ * The workspace holds one fp64 partial per tile and sample. */
+dpnorm_status dpnorm_exact(const void* A, const void* G, dpnorm_dtype dt, int64_t B, int64_t T, int64_t d,
+                           int64_t p, dpnorm_route route, float* n, int accumulate, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* Clip factors (note: 方法详解 › 整体框架): c[i] = min(C / sqrt(n[i]), 1),
  * with n = 0 giving 1, n = +inf giving 0 and NaN propagating. C must be

@@ -23,7 +23,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["DpnormError", "hutch", "hutch_grouped", "clip_factors", "hutchpp_split", "KernelTimer", "lib"]
+__all__ = ["DpnormError", "hutch", "hutch_grouped", "hutchpp", "exact", "clip_factors", "hutchpp_split", "KernelTimer",
+           "lib"]
 
 
 class DpnormError(RuntimeError):
@@ -181,6 +182,66 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
         _check(L.dpnorm_hutch_grouped_traced(*args, C.byref(tr)), "dpnorm_hutch_grouped_traced")
         timer._record(tr)
     return (n, c) if c is not None else n
+
+
+def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, k: Optional[int] = None,
+            out: Optional[torch.Tensor] = None, accumulate: bool = False, return_parts: bool = False):
+    """Hutch++ estimate with total budget k (dpnorm_hutchpp).
+
+    S [p][m_s] is the sketch and P [p][m_t] the tail projection, with
+    (m_s, m_t) = hutchpp_split(k); by default k = 2 m_s + m_t from the shapes. Returns n [B], or (n, head, tail, rank) with return_parts.
+    """
+    _need(A, "A", 3)
+    dtype, device = A.dtype, A.device
+    _need(G, "G", 3, dtype)
+    _need(S, "S", 2, dtype)
+    _need(P, "P", 2, dtype)
+    B, T, d = A.shape
+    p = G.shape[2]
+    if G.shape[:2] != (B, T) or S.shape[0] != p or P.shape[0] != p:
+        raise ValueError("shapes must be A [B][T][d], G [B][T][p], S [p][m_s], P [p][m_t]")
+    if k is None:
+        k = 2 * S.shape[1] + P.shape[1]
+    ms, mt = hutchpp_split(k)
+    if S.shape[1] != ms or P.shape[1] != mt:
+        raise ValueError(f"budget {k} needs S with {ms} and P with {mt} columns")
+    L = lib()
+    nbytes = C.c_size_t(0)
+    _check(L.dpnorm_hutchpp_workspace(_code(dtype), B, T, d, p, k, C.byref(nbytes)), "dpnorm_hutchpp_workspace")
+    n = _out(out, B, device, accumulate)
+    head = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
+    tail = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
+    rank = torch.empty(B, dtype=torch.int32, device=device) if return_parts else None
+    ws, wsp = _workspace(nbytes.value, device)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    _check(L.dpnorm_hutchpp(A.data_ptr(), G.data_ptr(), S.data_ptr(), P.data_ptr(), _code(dtype), B, T, d, p, k,
+                            n.data_ptr(), int(accumulate), ptr(head), ptr(tail), ptr(rank), wsp, nbytes.value,
+                            _stream(device)), "dpnorm_hutchpp")
+    return (n, head, tail, rank) if return_parts else n
+
+
+_ROUTES = {"auto": _lib.EXACT_AUTO, "explicit": _lib.EXACT_EXPLICIT, "gram": _lib.EXACT_GRAM}
+
+
+def exact(A: torch.Tensor, G: torch.Tensor, route: str = "auto", out: Optional[torch.Tensor] = None,
+          accumulate: bool = False) -> torch.Tensor:
+    """Exact n_i = ||A_i^T G_i||_F^2 (dpnorm_exact); route 'auto', 'explicit' or 'gram'."""
+    _need(A, "A", 3)
+    dtype, device = A.dtype, A.device
+    _need(G, "G", 3, dtype)
+    B, T, d = A.shape
+    p = G.shape[2]
+    if G.shape[:2] != (B, T):
+        raise ValueError("A and G must be [B][T][*]")
+    r = _ROUTES[route]
+    L = lib()
+    nbytes = C.c_size_t(0)
+    _check(L.dpnorm_exact_workspace(_code(dtype), B, T, d, p, r, C.byref(nbytes)), "dpnorm_exact_workspace")
+    n = _out(out, B, device, accumulate)
+    ws, wsp = _workspace(nbytes.value, device)
+    _check(L.dpnorm_exact(A.data_ptr(), G.data_ptr(), _code(dtype), B, T, d, p, r, n.data_ptr(), int(accumulate), wsp,
+                          nbytes.value, _stream(device)), "dpnorm_exact")
+    return n
 
 
 def clip_factors(n: torch.Tensor, C_clip: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:

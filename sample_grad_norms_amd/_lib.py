@@ -49,6 +49,11 @@ SIGNATURES = {
                               _vp], C.c_int),
     "dpnorm_hutch_grouped_traced": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32, _vp,
                                      _sz, _vp, C.POINTER(Trace)], C.c_int),
+    "dpnorm_hutchpp_workspace": ([C.c_int, _i64, _i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
+    "dpnorm_hutchpp": ([_vp, _vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _vp, _vp, _vp,
+                        _sz, _vp], C.c_int),
+    "dpnorm_exact_workspace": ([C.c_int, _i64, _i64, _i64, _i64, C.c_int, C.POINTER(_sz)], C.c_int),
+    "dpnorm_exact": ([_vp, _vp, C.c_int, _i64, _i64, _i64, _i64, C.c_int, _vp, C.c_int, _vp, _sz, _vp], C.c_int),
     "dpnorm_clip_factors": ([_vp, _i64, _f32, _vp, _vp], C.c_int),
     "dpnorm_event_create": ([C.POINTER(_vp)], C.c_int),
     "dpnorm_event_destroy": ([_vp], C.c_int),

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = [
     "kernels_hutch.hip",
+    "kernels_hutchpp.hip",
+    "kernels_exact.hip",
     "dpnorm.cpp",
 ]
 

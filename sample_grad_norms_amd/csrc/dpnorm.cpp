@@ -383,6 +383,91 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
   return hip_status(he);
 }
 
+// ---------------------------------------------------------------------------
+// Hutch++ (three passes, basis and tail in between)
+// ---------------------------------------------------------------------------
+constexpr float kRankTau = 1e-5f;  // column kept when residual > tau * largest sketch column norm
+constexpr int kMaxSketch = 32;      // sketch columns handled by the basis kernel
+
+struct HppCall {
+  int64_t ms = 0, mt = 0;
+  PassPlan p1, p2, p3;
+  std::vector<PassLayer> l1, l2, l3;
+  size_t off_ys = 0, off_x = 0, off_qd = 0, off_v = 0, off_w3 = 0, off_rank = 0;
+  int NC1 = 0, NC3 = 0;
+  size_t bytes = 0;
+};
+
+dpnorm_status build_hutchpp(const void* A, const void* G, const void* S, const void* P, dpnorm_dtype dt, int64_t B,
+                            int64_t T, int64_t d, int64_t p, int64_t k, bool need_ptrs, HppCall& hc) {
+  if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
+  dpnorm_status st = check_dims(dt, B, T, d, p);
+  if (st != DPNORM_OK) return st;
+  if (k < 3 || k > 96) return DPNORM_ERR_SIZE;
+  hc.ms = (k + 2) / 3;
+  hc.mt = k - 2 * hc.ms;
+  if (hc.mt < 1 || hc.ms > kMaxSketch || hc.ms + hc.mt > kMaxK) return DPNORM_ERR_SIZE;
+  if (need_ptrs) {
+    if (!A || !G || !S || !P) return DPNORM_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(G, 16) || !aligned(S, esize(dt)) || !aligned(P, esize(dt))) return DPNORM_ERR_ALIGN;
+  }
+  const bool bf16 = dt == DPNORM_BF16;
+  const int src = bf16 ? SRC_BF16 : SRC_F32;
+  const int ncb1 = ncb_of(hc.ms), ncb3 = ncb_of(hc.ms + hc.mt);
+  hc.NC1 = 16 * ncb1;
+  hc.NC3 = 16 * ncb3;
+  Bump bump;
+  // pass 1: Y_S = A^T (G S)   [B][d][NC1]
+  hc.l1.resize(1);
+  hc.l1[0].X1 = G; hc.l1[0].w1 = p; hc.l1[0].X2 = A; hc.l1[0].w2 = d;
+  hc.l1[0].wsrc = S; hc.l1[0].wsrc_type = src; hc.l1[0].ld = hc.ms; hc.l1[0].ncols = (int)hc.ms;
+  hc.p1.bf16 = bf16; hc.p1.NCB = ncb1; hc.p1.HL = 1; hc.p1.B = B; hc.p1.T = T; hc.p1.store = true;
+  plan_pass(hc.p1, hc.l1, bump);
+  hc.off_ys = bump.take((size_t)B * d * hc.NC1 * 4);
+  // pass 2: X = G^T (A Y_S) = O S   [B][p][NC1]
+  hc.l2.resize(1);
+  hc.l2[0].X1 = A; hc.l2[0].w1 = d; hc.l2[0].X2 = G; hc.l2[0].w2 = p;
+  hc.l2[0].wsrc_type = SRC_F32; hc.l2[0].ld = hc.NC1; hc.l2[0].ncols = (int)hc.ms;
+  hc.l2[0].nsamples = (int)B; hc.l2[0].wsrc_stride_b = d * hc.NC1;
+  hc.p2.bf16 = bf16; hc.p2.NCB = ncb1; hc.p2.HL = 2; hc.p2.B = B; hc.p2.T = T; hc.p2.store = true;
+  plan_pass(hc.p2, hc.l2, bump);
+  hc.off_x = bump.take((size_t)B * p * hc.NC1 * 4);
+  // basis scratch and the head/tail matrix W3 = [Q | P']   [B][p][NC3]
+  hc.off_qd = bump.take((size_t)B * hc.ms * p * 8);
+  hc.off_v = bump.take((size_t)B * p * 8);
+  hc.off_w3 = bump.take((size_t)B * p * hc.NC3 * 4);
+  hc.off_rank = bump.take((size_t)B * 4);
+  // pass 3: head = ||A^T G Q||^2, tail = ||A^T G P'||^2
+  hc.l3.resize(1);
+  hc.l3[0].X1 = G; hc.l3[0].w1 = p; hc.l3[0].X2 = A; hc.l3[0].w2 = d;
+  hc.l3[0].wsrc_type = SRC_F32; hc.l3[0].ld = hc.NC3; hc.l3[0].ncols = (int)(hc.ms + hc.mt);
+  hc.l3[0].nsamples = (int)B; hc.l3[0].wsrc_stride_b = p * hc.NC3; hc.l3[0].split = (int)hc.ms;
+  hc.p3.bf16 = bf16; hc.p3.NCB = ncb3; hc.p3.HL = 2; hc.p3.B = B; hc.p3.T = T; hc.p3.store = false;
+  plan_pass(hc.p3, hc.l3, bump);
+  hc.bytes = align_up(bump.off);
+  return DPNORM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Exact
+// ---------------------------------------------------------------------------
+dpnorm_status exact_plan(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, dpnorm_route route, bool& gram,
+                         int32_t& slots, size_t& bytes) {
+  if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
+  if (route != DPNORM_EXACT_AUTO && route != DPNORM_EXACT_EXPLICIT && route != DPNORM_EXACT_GRAM)
+    return DPNORM_ERR_DTYPE;
+  const dpnorm_status st = check_dims(dt, B, T, d, p);
+  if (st != DPNORM_OK) return st;
+  gram = route == DPNORM_EXACT_GRAM || (route == DPNORM_EXACT_AUTO && (double)d * (double)p > (double)T * (double)T);
+  int32_t tu = 0, tv = 0;
+  const int64_t e = dt == DPNORM_BF16 ? 128 : 64;
+  const int64_t tiles = gram ? ((T + 127) / 128) * ((T + 127) / 128 + 1) / 2 : ((d + e - 1) / e) * ((p + e - 1) / e);
+  if (tiles * B >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;
+  exact_tiles(dt == DPNORM_BF16, gram, T, d, p, tu, tv, slots);
+  bytes = align_up(sizeof(double2) * (size_t)B * slots);
+  return DPNORM_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -462,6 +547,98 @@ dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L,
                                           void* ws, size_t ws_bytes, hipStream_t stream, dpnorm_trace* trace) {
   if (!trace) return DPNORM_ERR_NULL;
   return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, trace);
+}
+
+dpnorm_status dpnorm_hutchpp_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, int64_t k,
+                                       size_t* bytes) {
+  if (!bytes) return DPNORM_ERR_NULL;
+  HppCall hc;
+  const dpnorm_status st = build_hutchpp(nullptr, nullptr, nullptr, nullptr, dt, B, T, d, p, k, false, hc);
+  if (st != DPNORM_OK) return st;
+  *bytes = hc.bytes;
+  return DPNORM_OK;
+}
+
+dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const void* P, dpnorm_dtype dt, int64_t B,
+                             int64_t T, int64_t d, int64_t p, int64_t k, float* n, int accumulate, float* head,
+                             float* tail, int32_t* rank, void* ws, size_t ws_bytes, hipStream_t stream) {
+  HppCall hc;
+  dpnorm_status st = build_hutchpp(A, G, S, P, dt, B, T, d, p, k, true, hc);
+  if (st != DPNORM_OK) return st;
+  if (!n) return DPNORM_ERR_NULL;
+  if (accumulate != 0 && accumulate != 1) return DPNORM_ERR_VALUE;
+  if (!aligned(n, 4) || (head && !aligned(head, 4)) || (tail && !aligned(tail, 4)) || (rank && !aligned(rank, 4)))
+    return DPNORM_ERR_ALIGN;
+  if (!ws) return DPNORM_ERR_NULL;
+  if (ws_bytes < hc.bytes) return DPNORM_ERR_WORKSPACE;
+  if (!aligned(ws, kAlign)) return DPNORM_ERR_ALIGN;
+  const size_t nb = (size_t)B * 4, e = esize(dt);
+  const size_t sa = (size_t)B * T * d * e, sg = (size_t)B * T * p * e;
+  const size_t ss = (size_t)p * hc.ms * e, sp = (size_t)p * hc.mt * e;
+  const void* outs[4] = {n, head, tail, rank};
+  for (int j = 0; j < 4; ++j) {
+    const void* o = outs[j];
+    if (!o) continue;
+    if (overlaps(o, nb, A, sa) || overlaps(o, nb, G, sg) || overlaps(o, nb, S, ss) || overlaps(o, nb, P, sp) ||
+        overlaps(o, nb, ws, hc.bytes))
+      return DPNORM_ERR_VALUE;
+    for (int q = j + 1; q < 4; ++q)
+      if (outs[q] && overlaps(o, nb, outs[q], nb)) return DPNORM_ERR_VALUE;
+  }
+  char* base = (char*)ws;
+  hc.l1[0].Yout = (float*)(base + hc.off_ys);
+  hc.l2[0].wsrc = base + hc.off_ys;
+  hc.l2[0].Yout = (float*)(base + hc.off_x);
+  hc.l3[0].wsrc = base + hc.off_w3;
+  float* W3 = (float*)(base + hc.off_w3);
+  int32_t* rk = (int32_t*)(base + hc.off_rank);
+  Tracer tr;
+  hipError_t he = run_pass(hc.p1, hc.l1, base, stream, tr);
+  if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr);
+  if (he == hipSuccess)
+    he = launch_hpp_basis((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.ms, kRankTau,
+                          (double*)(base + hc.off_qd), (double*)(base + hc.off_v), W3, hc.NC3, rk, stream);
+  if (he == hipSuccess)
+    he = launch_hpp_tail(P, dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, (int)hc.mt, (int)B, (int)p, (int)hc.ms,
+                         (int)hc.mt, (const double*)(base + hc.off_qd), rk, W3, hc.NC3, stream);
+  if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr);
+  if (he == hipSuccess)
+    he = launch_finish((const double2*)(base + hc.p3.off_partials), (int32_t)B, hc.p3.slots, n, accumulate, head,
+                       tail, nullptr, 1.f, 0, stream);
+  if (he == hipSuccess && rank) he = hipMemcpyAsync(rank, rk, nb, hipMemcpyDeviceToDevice, stream);
+  return hip_status(he);
+}
+
+dpnorm_status dpnorm_exact_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, dpnorm_route route,
+                                     size_t* bytes) {
+  if (!bytes) return DPNORM_ERR_NULL;
+  bool gram = false;
+  int32_t slots = 0;
+  return exact_plan(dt, B, T, d, p, route, gram, slots, *bytes);
+}
+
+dpnorm_status dpnorm_exact(const void* A, const void* G, dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p,
+                           dpnorm_route route, float* n, int accumulate, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  bool gram = false;
+  int32_t slots = 0;
+  size_t bytes = 0;
+  dpnorm_status st = exact_plan(dt, B, T, d, p, route, gram, slots, bytes);
+  if (st != DPNORM_OK) return st;
+  if (!A || !G || !n || !ws) return DPNORM_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(G, 16) || !aligned(n, 4) || !aligned(ws, kAlign)) return DPNORM_ERR_ALIGN;
+  if (accumulate != 0 && accumulate != 1) return DPNORM_ERR_VALUE;
+  if (ws_bytes < bytes) return DPNORM_ERR_WORKSPACE;
+  const size_t nb = (size_t)B * 4, e = esize(dt);
+  if (overlaps(n, nb, A, (size_t)B * T * d * e) || overlaps(n, nb, G, (size_t)B * T * p * e) ||
+      overlaps(n, nb, ws, bytes))
+    return DPNORM_ERR_VALUE;
+  hipError_t he = launch_exact(A, G, dt == DPNORM_BF16, gram, (int32_t)B, (int32_t)T, (int32_t)d, (int32_t)p,
+                               (double2*)ws, stream);
+  if (he == hipSuccess)
+    he = launch_finish((const double2*)ws, (int32_t)B, slots, n, accumulate, nullptr, nullptr, nullptr, 1.f, 0,
+                       stream);
+  return hip_status(he);
 }
 
 dpnorm_status dpnorm_clip_factors(const float* n, int64_t B, float C, float* c, hipStream_t stream) {

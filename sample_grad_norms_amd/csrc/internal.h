@@ -87,4 +87,17 @@ hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, floa
                          float* head, float* tail, float* c, float C, int with_clip, hipStream_t s);
 hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s);
 
+// Hutch++: orthonormal basis of the sketch X [B][p][ldx] (first m columns)
+// into W3 [B][p][ldw] columns 0..m-1 (kept columns first, then zeros), rank
+// per sample; then P' = P - Q (Q^T P) into columns m..m+mt-1.
+hipError_t launch_hpp_basis(const float* X, int ldx, int B, int p, int m, float tau, double* Qd, double* vbuf,
+                            float* W3, int ldw, int32_t* rank, hipStream_t s);
+hipError_t launch_hpp_tail(const void* P, int ptype, int ldp, int B, int p, int m, int mt, const double* Qd,
+                           const int32_t* rank, float* W3, int ldw, hipStream_t s);
+
+// Exact squared norms: one fp64 partial per tile into partials [B][slots].
+void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots);
+hipError_t launch_exact(const void* A, const void* G, bool bf16, bool gram, int32_t B, int32_t T, int32_t d,
+                        int32_t p, double2* partials, hipStream_t s);
+
 }  // namespace dpn

@@ -1,0 +1,323 @@
+// Exact per-sample squared norm ||A_i^T G_i||_F^2, the comparator of the
+// estimators ('Efficient DP-SGD for LLMs with Randomized Clipping',
+// papernotes.org note, 研究背景与动机 and 相关工作: explicit per-sample
+// gradients cost O(T d p), ghost clipping works on T x T Gram matrices;
+// gist.science/nl summary, Complexiteitsreductie).
+//
+// Explicit route: W_i = A_i^T G_i is formed tile by tile in MFMA
+// accumulators (contraction over T, both operands transposed in registers)
+// and squared in place; nothing of size d x p is stored.
+// Gram route: n_i = <A_i A_i^T, G_i G_i^T>_F; a work group forms matching
+// 128 x 128 tiles of both Gram matrices (contractions over d and p, operands
+// read row-major as stored) and sums their elementwise product; tiles below
+// the diagonal count twice by symmetry and nothing of size T x T is stored.
+// Both write one fp64 partial per tile; the per-sample finisher adds them in
+// a fixed order.
+#include "device_common.h"
+#include "internal.h"
+
+namespace dpn {
+
+struct ExactArgs {
+  const void* A;
+  const void* G;
+  int32_t B, T, d, p;
+  int32_t tu, tv;       // explicit: tiles along d and p; gram: tu = tiles along T
+  int32_t n_items;
+  int32_t slots;        // partial slots per sample
+  double2* partials;
+};
+
+// ---------------------------------------------------------------------------
+// Explicit, bf16: one wave per 128 (d) x 128 (p) tile of W_i. Per 32-row chunk
+// a lane loads 8 rows of 8 consecutive columns of A and of G, transposes both
+// 8 x 8 blocks so T runs along the K slots, and issues the 64 MFMAs of the
+// tile; the next chunk's loads are in flight meanwhile.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) k_exact_explicit_bf16(ExactArgs a) {
+  const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
+  const int per_i = a.tu * a.tv;
+  const int i = item / per_i, rem = item - i * per_i;
+  const int tu = rem / a.tv, tv = rem - tu * a.tv;
+  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const int T = a.T, d = a.d, p = a.p;
+  const int ua = 128 * tu + 8 * n, vb = 128 * tv + 8 * n;
+  const bool aok = ua < d, gok = vb < p;
+  const uint16_t* Ap = (const uint16_t*)a.A + (int64_t)i * T * d + ua;
+  const uint16_t* Gp = (const uint16_t*)a.G + (int64_t)i * T * p + vb;
+  const int nch = (T + 31) >> 5;
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[e][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  auto load = [&](int c, uint4 (&ra)[8], uint4 (&rg)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int t = 32 * c + slot_row(g, s);
+      const bool tok = c < nch && t < T;
+      ra[s] = (tok && aok) ? ldg16(Ap + (int64_t)t * d) : z;
+      rg[s] = (tok && gok) ? ldg16(Gp + (int64_t)t * p) : z;
+    }
+  };
+  uint4 ra[8], rg[8];
+  load(0, ra, rg);
+  for (int c = 0; c < nch; ++c) {
+    uint4 na[8], ng[8];
+    load(c + 1, na, ng);
+    uint4 oa[8], og[8];
+    transpose8x8_bf16(ra, oa);
+    transpose8x8_bf16(rg, og);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int f = 0; f < 8; ++f) acc[e][f] = mfma_bf16(oa[e], og[f], acc[e][f]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      ra[s] = na[s];
+      rg[s] = ng[s];
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double y = (double)acc[e][f][r];
+        ss += y * y;
+      }
+  ss = wave_sum(ss);
+  if (lane == 0) a.partials[(int64_t)i * a.slots + rem] = make_double2(ss, 0.0);
+}
+
+// ---------------------------------------------------------------------------
+// Explicit, fp32: one wave per 64 x 64 tile; a lane's float4 of 4 consecutive
+// columns of A (of G) at row 4 st + l/16 feeds the four MFMAs of its column
+// offset, so no transpose is needed.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) k_exact_explicit_f32(ExactArgs a) {
+  const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
+  const int per_i = a.tu * a.tv;
+  const int i = item / per_i, rem = item - i * per_i;
+  const int tu = rem / a.tv, tv = rem - tu * a.tv;
+  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const int T = a.T, d = a.d, p = a.p;
+  const int ua = 64 * tu + 4 * n, vb = 64 * tv + 4 * n;
+  const bool aok = ua < d, gok = vb < p;
+  const float* Ap = (const float*)a.A + (int64_t)i * T * d + ua;
+  const float* Gp = (const float*)a.G + (int64_t)i * T * p + vb;
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[e][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int t0 = 0; t0 < T; t0 += 4) {
+    const int t = t0 + g;
+    const float4 x = (t < T && aok) ? ldg_f32x4(Ap + (int64_t)t * d) : z;
+    const float4 y = (t < T && gok) ? ldg_f32x4(Gp + (int64_t)t * p) : z;
+    const float xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[e][f] = mfma_f32(xv[e], yv[f], acc[e][f]);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double v = (double)acc[e][f][r];
+        ss += v * v;
+      }
+  ss = wave_sum(ss);
+  if (lane == 0) a.partials[(int64_t)i * a.slots + rem] = make_double2(ss, 0.0);
+}
+
+// Lower-triangular tile pair (bt >= bs) of linear index j.
+__device__ __forceinline__ void tri_pair(int j, int& bt, int& bs) {
+  int t = (int)((sqrt(8.0 * j + 1.0) - 1.0) * 0.5);
+  while ((t + 1) * (t + 2) / 2 <= j) ++t;
+  while (t * (t + 1) / 2 > j) --t;
+  bt = t;
+  bs = j - t * (t + 1) / 2;
+}
+
+// ---------------------------------------------------------------------------
+// Gram, bf16: work group = 4 waves on a 128 (t) x 128 (s) tile pair, wave
+// (wy, wx) on 64 x 64. K steps of 32 over d (then p) read both operands
+// straight from the row-major rows of A (of G).
+// ---------------------------------------------------------------------------
+template <typename LoadOp>
+__device__ __forceinline__ void gram_tile_bf16(const uint16_t* M, int T, int w, int trow0, int srow0,
+                                               f32x4_t (&acc)[4][4], int n, int g) {
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int nks = (w + 31) >> 5;
+  for (int ks = 0; ks < nks; ++ks) {
+    const int col = 32 * ks + 8 * g;
+    const bool cok = col < w;
+    uint4 ta[4], sb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tr = trow0 + 16 * m + n, sr = srow0 + 16 * m + n;
+      ta[m] = (cok && tr < T) ? LoadOp()(M + (int64_t)tr * w + col) : z;
+      sb[m] = (cok && sr < T) ? LoadOp()(M + (int64_t)sr * w + col) : z;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[m][q] = mfma_bf16(ta[m], sb[q], acc[m][q]);
+  }
+}
+
+struct LoadG16 {
+  __device__ __forceinline__ uint4 operator()(const void* p) const { return ldg16(p); }
+};
+
+__global__ void __launch_bounds__(256) k_exact_gram_bf16(ExactArgs a) {
+  __shared__ double red[4];
+  const int per_i = a.tu * (a.tu + 1) / 2;
+  const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
+  const int i = item / per_i, j = item - i * per_i;
+  int bt, bs;
+  tri_pair(j, bt, bs);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+  const int trow0 = 128 * bt + 64 * (wv >> 1), srow0 = 128 * bs + 64 * (wv & 1);
+  const int T = a.T;
+  f32x4_t ka[4][4], kg[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ka[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      kg[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  gram_tile_bf16<LoadG16>((const uint16_t*)a.A + (int64_t)i * T * a.d, T, a.d, trow0, srow0, ka, n, g);
+  gram_tile_bf16<LoadG16>((const uint16_t*)a.G + (int64_t)i * T * a.p, T, a.p, trow0, srow0, kg, n, g);
+  double ss = 0.0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss += (double)ka[m][q][r] * (double)kg[m][q][r];
+  ss = wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double wgt = bs < bt ? 2.0 : 1.0;
+    a.partials[(int64_t)i * a.slots + j] = make_double2(wgt * ((red[0] + red[1]) + (red[2] + red[3])), 0.0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gram, fp32: same tiling with v_mfma_f32_16x16x4f32; a lane's float4 of 4
+// consecutive columns feeds four MFMAs (K slot l / 16 is column 16 ks + 4 (l/16) + q).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void gram_tile_f32(const float* M, int T, int w, int trow0, int srow0,
+                                              f32x4_t (&acc)[4][4], int n, int g) {
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nks = (w + 15) >> 4;
+  for (int ks = 0; ks < nks; ++ks) {
+    const int col = 16 * ks + 4 * g;
+    const bool cok = col < w;
+    float4 ta[4], sb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tr = trow0 + 16 * m + n, sr = srow0 + 16 * m + n;
+      ta[m] = (cok && tr < T) ? ldg_f32x4(M + (int64_t)tr * w + col) : z;
+      sb[m] = (cok && sr < T) ? ldg_f32x4(M + (int64_t)sr * w + col) : z;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[m][q] = mfma_f32(ta[m].x, sb[q].x, acc[m][q]);
+        acc[m][q] = mfma_f32(ta[m].y, sb[q].y, acc[m][q]);
+        acc[m][q] = mfma_f32(ta[m].z, sb[q].z, acc[m][q]);
+        acc[m][q] = mfma_f32(ta[m].w, sb[q].w, acc[m][q]);
+      }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_exact_gram_f32(ExactArgs a) {
+  __shared__ double red[4];
+  const int per_i = a.tu * (a.tu + 1) / 2;
+  const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
+  const int i = item / per_i, j = item - i * per_i;
+  int bt, bs;
+  tri_pair(j, bt, bs);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+  const int trow0 = 128 * bt + 64 * (wv >> 1), srow0 = 128 * bs + 64 * (wv & 1);
+  const int T = a.T;
+  f32x4_t ka[4][4], kg[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ka[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      kg[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  gram_tile_f32((const float*)a.A + (int64_t)i * T * a.d, T, a.d, trow0, srow0, ka, n, g);
+  gram_tile_f32((const float*)a.G + (int64_t)i * T * a.p, T, a.p, trow0, srow0, kg, n, g);
+  double ss = 0.0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss += (double)ka[m][q][r] * (double)kg[m][q][r];
+  ss = wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double wgt = bs < bt ? 2.0 : 1.0;
+    a.partials[(int64_t)i * a.slots + j] = make_double2(wgt * ((red[0] + red[1]) + (red[2] + red[3])), 0.0);
+  }
+}
+
+// Work decomposition shared with the host: explicit tiles are 128 x 128
+// (bf16) or 64 x 64 (fp32) of W_i; Gram tiles are 128 x 128 pairs (t >= s).
+void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots) {
+  if (gram) {
+    tu = (int32_t)((T + 127) / 128);
+    tv = tu;
+    slots = tu * (tu + 1) / 2;
+  } else {
+    const int64_t e = bf16 ? 128 : 64;
+    tu = (int32_t)((d + e - 1) / e);
+    tv = (int32_t)((p + e - 1) / e);
+    slots = tu * tv;
+  }
+}
+
+hipError_t launch_exact(const void* A, const void* G, bool bf16, bool gram, int32_t B, int32_t T, int32_t d,
+                        int32_t p, double2* partials, hipStream_t s) {
+  ExactArgs a;
+  a.A = A;
+  a.G = G;
+  a.B = B;
+  a.T = T;
+  a.d = d;
+  a.p = p;
+  exact_tiles(bf16, gram, T, d, p, a.tu, a.tv, a.slots);
+  a.n_items = B * a.slots;
+  a.partials = partials;
+  if (gram) {
+    if (bf16) hipLaunchKernelGGL(k_exact_gram_bf16, dim3(a.n_items), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_exact_gram_f32, dim3(a.n_items), dim3(256), 0, s, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL(k_exact_explicit_bf16, dim3(a.n_items), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_exact_explicit_f32, dim3(a.n_items), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dpn

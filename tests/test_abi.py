@@ -159,3 +159,38 @@ def test_event_helpers_reject_null(lib):
     assert lib.dpnorm_event_synchronize(None) == _lib.ERR_NULL
     ms = C.c_float(0)
     assert lib.dpnorm_event_elapsed_ms(None, None, C.byref(ms)) == _lib.ERR_NULL
+
+
+def test_hutchpp_checks(lib):
+    nb = C.c_size_t(0)
+    assert lib.dpnorm_hutchpp_workspace(_lib.BF16, 2, 100, 64, 32, 32, C.byref(nb)) == _lib.OK and nb.value > 0
+    for k in (2, 97):
+        assert lib.dpnorm_hutchpp_workspace(_lib.BF16, 2, 100, 64, 32, k, C.byref(nb)) == _lib.ERR_SIZE
+    lib.dpnorm_hutchpp_workspace(_lib.BF16, 2, 100, 64, 32, 32, C.byref(nb))
+    S_ADDR = 0x600000
+    args = [A_ADDR, G_ADDR, S_ADDR, P_ADDR, _lib.BF16, 2, 100, 64, 32, 32, N_ADDR, 0, None, None, None]
+    assert lib.dpnorm_hutchpp(*args, WS_ADDR, nb.value - 1, None) == _lib.ERR_WORKSPACE
+    bad = list(args); bad[2] = None
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_NULL
+    bad = list(args); bad[12] = N_ADDR      # head aliases n
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_VALUE
+    bad = list(args); bad[4] = 9
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_DTYPE
+    bad = list(args); bad[11] = 3
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_VALUE
+
+
+def test_exact_checks(lib):
+    nb = C.c_size_t(0)
+    for route in (_lib.EXACT_AUTO, _lib.EXACT_EXPLICIT, _lib.EXACT_GRAM):
+        assert lib.dpnorm_exact_workspace(_lib.BF16, 2, 100, 64, 32, route, C.byref(nb)) == _lib.OK
+        assert nb.value > 0
+    assert lib.dpnorm_exact_workspace(_lib.BF16, 2, 100, 64, 32, 5, C.byref(nb)) == _lib.ERR_DTYPE
+    assert lib.dpnorm_exact_workspace(_lib.BF16, 2, 100, 60, 32, 0, C.byref(nb)) == _lib.ERR_SIZE
+    lib.dpnorm_exact_workspace(_lib.BF16, 2, 100, 64, 32, 0, C.byref(nb))
+    args = (A_ADDR, G_ADDR, _lib.BF16, 2, 100, 64, 32, _lib.EXACT_AUTO, N_ADDR, 0)
+    assert lib.dpnorm_exact(*args, WS_ADDR, nb.value - 1, None) == _lib.ERR_WORKSPACE
+    assert lib.dpnorm_exact(None, G_ADDR, _lib.BF16, 2, 100, 64, 32, 0, N_ADDR, 0, WS_ADDR, nb.value,
+                            None) == _lib.ERR_NULL
+    assert lib.dpnorm_exact(A_ADDR, G_ADDR, _lib.BF16, 2, 100, 64, 32, 0, A_ADDR, 0, WS_ADDR, nb.value,
+                            None) == _lib.ERR_VALUE
