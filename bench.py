@@ -3,14 +3,16 @@
 One step = one grouped Hutchinson call over the Llama-3.2-1B-shaped stack
 (16 decoder layers x {q, k, v, o, gate, up, down}, B = 4, T = 4096, k = 32,
 bf16 inputs, fp32 accumulation, an independent P per projection): G P, the
-split-free A^T (G P) contraction with its squared Frobenius norm, the
-per-sample layer sum over all 112 projections and the clip factors at C = 1.
-Inputs are synthetic, seeded, and resident in HBM before timing starts.
+A^T (G P) contraction with its squared Frobenius norm, the per-sample layer
+sum over all 112 projections and the clip factors at C = 1. Inputs are
+synthetic, seeded, and resident in HBM before timing starts.
 
-Prints one JSON line with the throughput (samples * tokens / s), the roofline
-of the dominant kernel (per-launch durations from HIP events the library
-records between its launches, on the stream the kernels run on) and the CPU
-oracle timed on a bounded sample of the same workload.
+Prints one JSON line: the throughput (samples * tokens / s), the roofline of
+the dominant kernel (per-launch durations from HIP events the library records
+between its launches, on the stream the kernels run on; HBM traffic from the
+committed rocprofv3 counter summary when it matches the current sources),
+the fp64 CPU oracle timed on the host over the same workload, and the other
+workloads (Hutch++, the exact comparator, single layers) under "extras".
 """
 from __future__ import annotations
 
@@ -24,8 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "per-sample norm-est samples·tokens/s (k=32, 1B-shape layers); % peak HBM BW"
+PROFILE = os.path.join(ROOT, "profiles", "rowproj_tcontract_llama1b_stack_B4_T4096_k32.md")
 
 
 def parse():
@@ -34,35 +38,152 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=4, help="decoder layers in the oracle's sample")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=16, help="decoder layers the CPU oracle runs over")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for hardware byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(layers, B, T, n_layers_total, n_sample_layers):
-    """The fp64 oracle on sample 0 of the first `n_sample_layers` decoder
-    layers (7 projections each), scaled to the whole step."""
-    import numpy as np
+def timed(fn, steps, warmup):
+    """Mean milliseconds per call of fn over `steps` calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def cpu_baseline(layers, B, T, n_layers):
+    """The fp64 oracle over the first `n_layers` decoder layers (7 projections
+    each, all B samples), one projection at a time; only the oracle's own
+    arithmetic is timed, the device-to-host copies and fp64 conversions are
+    not. Scaled to the 16-layer step when n_layers < 16."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    sub = layers[: 7 * n_sample_layers]
-    host = [(A[:1].cpu(), G[:1].cpu(), P.cpu()) for (A, G, P) in sub]
-    host = [(oracle.to_f64(A), oracle.to_f64(G), oracle.to_f64(P)) for (A, G, P) in host]
+    spent = 0.0
+    parts = []
+    for (A, G, P) in layers[: 7 * n_layers]:
+        a, g, p = oracle.to_f64(A), oracle.to_f64(G), oracle.to_f64(P)
+        t0 = time.perf_counter()
+        parts.append(oracle.hutch(a, g, p))
+        spent += time.perf_counter() - t0
+        del a, g, p
     t0 = time.perf_counter()
-    parts = [oracle.hutch(A, G, P) for (A, G, P) in host]
-    tot = oracle.layer_sum(parts)
-    oracle.clip_factors(tot, 1.0)
-    dt = time.perf_counter() - t0
-    # one sample over n_sample_layers of the n_layers_total decoder layers
-    step_s = dt * B * (n_layers_total / n_sample_layers)
+    oracle.clip_factors(oracle.layer_sum(parts), 1.0)
+    spent += time.perf_counter() - t0
+    step_s = spent * 16 / n_layers
     return {"value": B * T / step_s, "unit": "samples·tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, sample 0 of {n_sample_layers} decoder layer(s) x 7 projections "
-                      f"(T={T}), {dt:.2f} s, scaled x{B * n_layers_total // n_sample_layers} to the step"}
+            "sample": f"fp64 numpy oracle over {n_layers} decoder layer(s) x 7 projections, all {B} samples, "
+                      f"T={T}: {spent:.2f} s of oracle arithmetic"
+                      + ("" if n_layers == 16 else f", scaled x{16 / n_layers:g} to the step")}
+
+
+def rotated(make, copies):
+    """`copies` independent input sets so that repeated calls stream from HBM
+    rather than from the 256 MB last-level cache."""
+    return [make(r) for r in range(copies)]
+
+
+def extras(args):
+    """Other workloads: single-layer Hutchinson, Hutch++ and the exact
+    comparator, each timed the same way."""
+    import torch
+    import sample_grad_norms_amd as dp
+    import workloads
+    dev = torch.device("cuda:0")
+    out = {}
+    steps, warm = max(5, args.steps // 2), 2
+
+    # single layer, bf16, B=8 T=1024 d=p=2048 k=32 (67 MB: rotate 6 copies)
+    sets = []
+    for r in range(6):
+        pr = workloads.config2(device=dev)
+        if r:
+            pr.A.copy_(torch.roll(pr.A, r, 1))
+            pr.G.copy_(torch.roll(pr.G, r, 1))
+        sets.append(pr)
+    B, T, d, p = 8, 1024, 2048, 2048
+    ws = torch.empty(dp.hutch_workspace(torch.bfloat16, B, T, d, p, 32), dtype=torch.uint8, device=dev)
+    wse = torch.empty(dp.exact_workspace(torch.bfloat16, B, T, d, p), dtype=torch.uint8, device=dev)
+    cyc = {"j": 0}
+
+    def h2():
+        pr = sets[cyc["j"] % len(sets)]
+        cyc["j"] += 1
+        dp.hutch(pr.A, pr.G, pr.P, workspace=ws)
+
+    def e2():
+        pr = sets[cyc["j"] % len(sets)]
+        cyc["j"] += 1
+        dp.exact(pr.A, pr.G, workspace=wse)
+    byt = B * T * (d + p) * 2
+    ms = timed(h2, steps, warm)
+    mse = timed(e2, max(3, steps // 4), 1)
+    out["single_layer_B8_T1024_d2048_p2048_k32"] = {
+        "hutch_ms": ms, "hutch_samples_tokens_per_s": B * T / (ms * 1e-3), "hutch_hbm_gbs": byt / ms / 1e6,
+        "exact_gram_ms": mse, "exact_gram_tflops": 2 * B * T * T * (d + p) / 2 / (mse * 1e-3) / 1e12}
+    del sets, ws, wse
+
+    # Hutch++ single layer, B=4 T=4096 d=p=2048, budget 32 (11/11/10); 134 MB: rotate 4 copies
+    sets = [workloads.config4(device=dev)]
+    for r in range(1, 4):
+        base = sets[0]
+        sets.append(workloads.Problem(torch.roll(base.A, r, 1).contiguous(), torch.roll(base.G, r, 1).contiguous(),
+                                      base.P, S=base.S, k=base.k))
+    B, T, d, p, k = 4, 4096, 2048, 2048, 32
+    ws = torch.empty(dp.hutchpp_workspace(torch.bfloat16, B, T, d, p, k), dtype=torch.uint8, device=dev)
+    wsh = torch.empty(dp.hutch_workspace(torch.bfloat16, B, T, d, p, k), dtype=torch.uint8, device=dev)
+    Pk = workloads.projection(p, k, 12345, dev, torch.bfloat16)
+
+    def h4():
+        pr = sets[cyc["j"] % len(sets)]
+        cyc["j"] += 1
+        dp.hutchpp(pr.A, pr.G, pr.S, pr.P, k=k, workspace=ws)
+
+    def h4h():
+        pr = sets[cyc["j"] % len(sets)]
+        cyc["j"] += 1
+        dp.hutch(pr.A, pr.G, Pk, workspace=wsh)
+    ms = timed(h4, steps, warm)
+    msh = timed(h4h, steps, warm)
+    byt = 3 * B * T * (d + p) * 2
+    out["hutchpp_B4_T4096_d2048_p2048_k32"] = {
+        "hutchpp_ms": ms, "hutchpp_samples_tokens_per_s": B * T / (ms * 1e-3),
+        "hutchpp_hbm_gbs_3_streams": byt / ms / 1e6, "hutch_same_inputs_ms": msh,
+        "hutchpp_over_hutch_time": ms / msh}
+    del sets, ws, wsh
+
+    # long context, B=1 T=32768 d=2048 p=8192: Hutchinson and the exact (explicit) comparator side by side
+    pr = workloads.config5(device=dev)
+    B, T, d, p = 1, 32768, 2048, 8192
+    ws = torch.empty(dp.hutch_workspace(torch.bfloat16, B, T, d, p, 32), dtype=torch.uint8, device=dev)
+    wse = torch.empty(dp.exact_workspace(torch.bfloat16, B, T, d, p), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: dp.hutch(pr.A, pr.G, pr.P, workspace=ws), steps, warm)
+    mse = timed(lambda: dp.exact(pr.A, pr.G, workspace=wse), max(3, steps // 4), 1)
+    fl = 2 * T * d * p
+    out["long_context_B1_T32768_d2048_p8192_k32"] = {
+        "hutch_ms": ms, "hutch_samples_tokens_per_s": B * T / (ms * 1e-3),
+        "hutch_hbm_gbs": B * T * (d + p) * 2 / ms / 1e6, "exact_explicit_ms": mse,
+        "exact_explicit_tflops": fl / (mse * 1e-3) / 1e12,
+        "exact_explicit_mfma_frac": fl / (mse * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "exact_over_hutch_time": mse / ms}
+    del pr, ws, wse
+
+    # tiny fp32 layer (latency)
+    pr = workloads.config1(device=dev)
+    ms = timed(lambda: dp.hutch_grouped([(pr.A, pr.G, pr.P)], C_clip=1.0), steps, warm)
+    mse = timed(lambda: dp.exact(pr.A, pr.G), steps, warm)
+    out["tiny_fp32_B2_T128_d64_p64_k8"] = {"hutch_clip_ms": ms, "exact_ms": mse}
+    return out
 
 
 def main():
@@ -73,6 +194,7 @@ def main():
         sys.exit(2)
     import torch
     import sample_grad_norms_amd as dp
+    from sample_grad_norms_amd import profiling
     import workloads
 
     dev = torch.device("cuda:0")
@@ -80,8 +202,7 @@ def main():
     B, T, k = 4, 4096, 32
     projs = [workloads.config3_projection(j, device=dev) for j in range(112)]
     layers = [(q.A, q.G, q.P) for q in projs]
-    ws_bytes = dp.hutch_grouped_workspace(layers, torch.bfloat16, B, T, k)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(dp.hutch_grouped_workspace(layers, torch.bfloat16, B, T, k), dtype=torch.uint8, device=dev)
     n = torch.empty(B, dtype=torch.float32, device=dev)
     c = torch.empty(B, dtype=torch.float32, device=dev)
     bytes_A = sum(A.numel() * A.element_size() for (A, _, _) in layers)
@@ -99,15 +220,7 @@ def main():
     def step(timer=None):
         dp.hutch_grouped(layers, out=n, C_clip=1.0, clip_out=c, workspace=ws, timer=timer)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    ms_step = timed(step, args.steps, args.warmup)
 
     # per-launch durations from the library's events (separate, traced steps)
     timer = dp.KernelTimer(64)
@@ -116,11 +229,12 @@ def main():
     for _ in range(n_trace):
         step(timer)
         for kind, ms in timer.last():
-            per_kind.setdefault(kind, []).append(ms)
-    avg = {kk: sum(v) / n_trace for kk, v in per_kind.items()}  # per step (prepare may run several times)
-    dom = max(("rowproj", "tcontract"), key=lambda kk: avg.get(kk, 0.0))
-    dom_bytes = bytes_G if dom == "rowproj" else bytes_A
-    achieved = dom_bytes / (avg[dom] * 1e-3) / 1e9
+            per_kind[kind] = per_kind.get(kind, 0.0) + ms
+    avg = {kk: v / n_trace for kk, v in per_kind.items()}  # per step (prepare runs several times per step)
+    alg = {"rowproj": bytes_G + bytes_P, "tcontract": bytes_A}
+    dom = max(alg, key=lambda kk: avg.get(kk, 0.0))
+    achieved = alg[dom] / (avg[dom] * 1e-3) / 1e9
+    traffic = profiling.read_traffic(PROFILE, "k_" + dom)
     value = B * T / (ms_step * 1e-3)
 
     rec = {
@@ -136,20 +250,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "Llama-3.2-1B-shaped linear stack, Hutchinson + layer sum + clip",
+        "config": {"workload": "Llama-3.2-1B-shaped linear stack: Hutchinson per-sample norms, layer sum, clip",
                    "layers": 16, "projections": 112, "B": B, "T": T, "k": k, "C": 1.0,
                    "algorithmic_bytes": alg_bytes},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "step_hbm_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_ms": avg,
-        "kernel_gbs": {"rowproj": bytes_G / (avg["rowproj"] * 1e-3) / 1e9,
-                       "tcontract": bytes_A / (avg["tcontract"] * 1e-3) / 1e9},
+        "kernel_gbs": {kk: alg[kk] / (avg[kk] * 1e-3) / 1e9 for kk in alg if kk in avg},
         "clip_fraction": float((c < 1.0).float().mean().item()),
     }
+    if not args.no_extras:
+        rec["extras"] = extras(args)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(layers, B, T, 16, args.cpu_layers)
+        rec["cpu_baseline"] = cpu_baseline(layers, B, T, max(1, min(16, args.cpu_layers)))
     print(json.dumps(rec), flush=True)
 
 

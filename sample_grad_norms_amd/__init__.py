@@ -24,7 +24,7 @@ import torch
 from . import _lib
 
 __all__ = ["DpnormError", "hutch", "hutch_grouped", "hutchpp", "exact", "clip_factors", "hutchpp_split", "KernelTimer",
-           "lib"]
+           "lib", "hutch_workspace", "hutch_grouped_workspace", "hutchpp_workspace", "exact_workspace"]
 
 
 class DpnormError(RuntimeError):
@@ -112,7 +112,7 @@ def _layer_array(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tensor
 
 
 def hutch(A: torch.Tensor, G: torch.Tensor, P: torch.Tensor, out: Optional[torch.Tensor] = None,
-          accumulate: bool = False) -> torch.Tensor:
+          accumulate: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """n_hat_i = ||A_i^T (G_i P)||_F^2 for every sample (dpnorm_hutch).
 
     A [B][T][d], G [B][T][p], P [p][k], all bfloat16 or all float32, on the
@@ -125,10 +125,16 @@ def hutch(A: torch.Tensor, G: torch.Tensor, P: torch.Tensor, out: Optional[torch
     _check(L.dpnorm_hutch_workspace(_code(dtype), B, T, A.shape[2], G.shape[2], k, C.byref(nbytes)),
            "dpnorm_hutch_workspace")
     n = _out(out, B, device, accumulate)
-    ws, wsp = _workspace(nbytes.value, device)
+    ws, wsp = _given_workspace(workspace, nbytes.value, device)
     _check(L.dpnorm_hutch(A.data_ptr(), G.data_ptr(), P.data_ptr(), _code(dtype), B, T, A.shape[2], G.shape[2], k,
                           n.data_ptr(), int(accumulate), wsp, nbytes.value, _stream(device)), "dpnorm_hutch")
     return n
+
+
+def hutch_workspace(dtype: torch.dtype, B: int, T: int, d: int, p: int, k: int) -> int:
+    nbytes = C.c_size_t(0)
+    _check(lib().dpnorm_hutch_workspace(_code(dtype), B, T, d, p, k, C.byref(nbytes)), "dpnorm_hutch_workspace")
+    return nbytes.value
 
 
 def hutch_grouped_workspace(layers, dtype: torch.dtype, B: int, T: int, k: int) -> int:
@@ -166,12 +172,7 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     c = None
     if C_clip is not None:
         c = _out(clip_out, B, device, False, "clip_out") if clip_out is not None else torch.empty_like(n)
-    if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes.value or not workspace.is_cuda:
-            raise ValueError("workspace too small")
-        ws, wsp = workspace, workspace.data_ptr()
-    else:
-        ws, wsp = _workspace(nbytes.value, device)
+    ws, wsp = _given_workspace(workspace, nbytes.value, device)
     args = (arr, len(layers), _code(dtype), B, T, k, n.data_ptr(), int(accumulate),
             c.data_ptr() if c is not None else None, float(C_clip) if C_clip is not None else 1.0,
             wsp, nbytes.value, _stream(device))
@@ -184,12 +185,39 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     return (n, c) if c is not None else n
 
 
+_ROUTES = {"auto": _lib.EXACT_AUTO, "explicit": _lib.EXACT_EXPLICIT, "gram": _lib.EXACT_GRAM}
+
+
+def _given_workspace(workspace: Optional[torch.Tensor], nbytes: int, device: torch.device):
+    if workspace is None:
+        return _workspace(nbytes, device)
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+    return workspace, workspace.data_ptr()
+
+
+def hutchpp_workspace(dtype: torch.dtype, B: int, T: int, d: int, p: int, k: int) -> int:
+    nbytes = C.c_size_t(0)
+    _check(lib().dpnorm_hutchpp_workspace(_code(dtype), B, T, d, p, k, C.byref(nbytes)), "dpnorm_hutchpp_workspace")
+    return nbytes.value
+
+
+def exact_workspace(dtype: torch.dtype, B: int, T: int, d: int, p: int, route: str = "auto") -> int:
+    nbytes = C.c_size_t(0)
+    _check(lib().dpnorm_exact_workspace(_code(dtype), B, T, d, p, _ROUTES[route], C.byref(nbytes)),
+           "dpnorm_exact_workspace")
+    return nbytes.value
+
+
 def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, k: Optional[int] = None,
-            out: Optional[torch.Tensor] = None, accumulate: bool = False, return_parts: bool = False):
+            out: Optional[torch.Tensor] = None, accumulate: bool = False, return_parts: bool = False,
+            workspace: Optional[torch.Tensor] = None):
     """Hutch++ estimate with total budget k (dpnorm_hutchpp).
 
     S [p][m_s] is the sketch and P [p][m_t] the tail projection, with
-    (m_s, m_t) = hutchpp_split(k); by default k = 2 m_s + m_t from the shapes. Returns n [B], or (n, head, tail, rank) with return_parts.
+    (m_s, m_t) = hutchpp_split(k); by default k = 2 m_s + m_t from the
+    shapes. Returns n [B], or (n, head, tail, rank) with return_parts.
+    ``workspace`` (uint8, GPU) may be passed to reuse one allocation.
     """
     _need(A, "A", 3)
     dtype, device = A.dtype, A.device
@@ -212,7 +240,7 @@ def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, 
     head = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
     tail = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
     rank = torch.empty(B, dtype=torch.int32, device=device) if return_parts else None
-    ws, wsp = _workspace(nbytes.value, device)
+    ws, wsp = _given_workspace(workspace, nbytes.value, device)
     ptr = lambda t: t.data_ptr() if t is not None else None
     _check(L.dpnorm_hutchpp(A.data_ptr(), G.data_ptr(), S.data_ptr(), P.data_ptr(), _code(dtype), B, T, d, p, k,
                             n.data_ptr(), int(accumulate), ptr(head), ptr(tail), ptr(rank), wsp, nbytes.value,
@@ -220,11 +248,8 @@ def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, 
     return (n, head, tail, rank) if return_parts else n
 
 
-_ROUTES = {"auto": _lib.EXACT_AUTO, "explicit": _lib.EXACT_EXPLICIT, "gram": _lib.EXACT_GRAM}
-
-
 def exact(A: torch.Tensor, G: torch.Tensor, route: str = "auto", out: Optional[torch.Tensor] = None,
-          accumulate: bool = False) -> torch.Tensor:
+          accumulate: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Exact n_i = ||A_i^T G_i||_F^2 (dpnorm_exact); route 'auto', 'explicit' or 'gram'."""
     _need(A, "A", 3)
     dtype, device = A.dtype, A.device
@@ -238,7 +263,7 @@ def exact(A: torch.Tensor, G: torch.Tensor, route: str = "auto", out: Optional[t
     nbytes = C.c_size_t(0)
     _check(L.dpnorm_exact_workspace(_code(dtype), B, T, d, p, r, C.byref(nbytes)), "dpnorm_exact_workspace")
     n = _out(out, B, device, accumulate)
-    ws, wsp = _workspace(nbytes.value, device)
+    ws, wsp = _given_workspace(workspace, nbytes.value, device)
     _check(L.dpnorm_exact(A.data_ptr(), G.data_ptr(), _code(dtype), B, T, d, p, r, n.data_ptr(), int(accumulate), wsp,
                           nbytes.value, _stream(device)), "dpnorm_exact")
     return n
