@@ -4,7 +4,9 @@
 //   A operand: lane l supplies 8 bf16 of row (l % 16) at K slots 8*(l/16)+j
 //   B operand: lane l supplies 8 bf16 of column (l % 16) at K slots 8*(l/16)+j
 //   C/D      : lane l holds rows 4*(l/16) + r, r = 0..3, of column (l % 16)
-// and for v_mfma_f32_16x16x4f32 one fp32 value per lane at K slot (l/16).
+// and for v_mfma_f32_16x16x4f32 one fp32 value per lane at K slot (l/16), with
+// the same C/D layout. (v_mfma_f64_16x16x4f64 differs: lane l holds rows
+// l/16 + 4 r, r = 0..3, of column l % 16.)
 // Only the pairing of A and B K slots matters for a contraction, so the
 // kernels are free to map any contraction index to a (group, element) slot
 // as long as both operands use the same map.

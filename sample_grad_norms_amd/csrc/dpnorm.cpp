@@ -120,7 +120,7 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
     pl.n2[l] = (int)(pl.B * pl.ubs[l] * pl.nsplit);
     pl.total2 += pl.n2[l];
     pl.slot_base[l] = pl.slots;
-    pl.slots += pl.ubs[l];
+    pl.slots += pl.ubs[l] * (pl.nsplit > 1 ? ysum_chunks(pl.cols2, pl.NCB) : 1);
     pl.n_pack[l] = (int)(L[l].nsamples * packed_units(pl, L[l].w1));
   }
   pl.off_recs = bump.take(sizeof(LayerRec) * nl);
@@ -393,7 +393,7 @@ struct HppCall {
   int64_t ms = 0, mt = 0;
   PassPlan p1, p2, p3;
   std::vector<PassLayer> l1, l2, l3;
-  size_t off_ys = 0, off_x = 0, off_qd = 0, off_v = 0, off_w3 = 0, off_rank = 0;
+  size_t off_ys = 0, off_x = 0, off_w3 = 0, off_rank = 0, off_qr = 0;
   int NC1 = 0, NC3 = 0;
   size_t bytes = 0;
 };
@@ -406,14 +406,15 @@ dpnorm_status build_hutchpp(const void* A, const void* G, const void* S, const v
   if (k < 3 || k > 96) return DPNORM_ERR_SIZE;
   hc.ms = (k + 2) / 3;
   hc.mt = k - 2 * hc.ms;
-  if (hc.mt < 1 || hc.ms > kMaxSketch || hc.ms + hc.mt > kMaxK) return DPNORM_ERR_SIZE;
+  if (hc.mt < 1 || hc.ms > kMaxSketch || hc.mt > kMaxSketch || 16 * ncb_of(hc.ms) + hc.mt > kMaxK)
+    return DPNORM_ERR_SIZE;
   if (need_ptrs) {
     if (!A || !G || !S || !P) return DPNORM_ERR_NULL;
     if (!aligned(A, 16) || !aligned(G, 16) || !aligned(S, esize(dt)) || !aligned(P, esize(dt))) return DPNORM_ERR_ALIGN;
   }
   const bool bf16 = dt == DPNORM_BF16;
   const int src = bf16 ? SRC_BF16 : SRC_F32;
-  const int ncb1 = ncb_of(hc.ms), ncb3 = ncb_of(hc.ms + hc.mt);
+  const int ncb1 = ncb_of(hc.ms), ncb3 = ncb_of(16 * ncb1 + hc.mt);  // W3 = [Q (16 ncb1 columns) | P']
   hc.NC1 = 16 * ncb1;
   hc.NC3 = 16 * ncb3;
   Bump bump;
@@ -432,16 +433,15 @@ dpnorm_status build_hutchpp(const void* A, const void* G, const void* S, const v
   hc.p2.bf16 = bf16; hc.p2.NCB = ncb1; hc.p2.HL = 2; hc.p2.B = B; hc.p2.T = T; hc.p2.store = true;
   plan_pass(hc.p2, hc.l2, bump);
   hc.off_x = bump.take((size_t)B * p * hc.NC1 * 4);
-  // basis scratch and the head/tail matrix W3 = [Q | P']   [B][p][NC3]
-  hc.off_qd = bump.take((size_t)B * hc.ms * p * 8);
-  hc.off_v = bump.take((size_t)B * p * 8);
+  // the head/tail matrix W3 = [Q | P']   [B][p][NC3]
   hc.off_w3 = bump.take((size_t)B * p * hc.NC3 * 4);
   hc.off_rank = bump.take((size_t)B * 4);
+  hc.off_qr = bump.take(hpp_qr_scratch_bytes(hc.NC1, (int)B, (int)p));
   // pass 3: head = ||A^T G Q||^2, tail = ||A^T G P'||^2
   hc.l3.resize(1);
   hc.l3[0].X1 = G; hc.l3[0].w1 = p; hc.l3[0].X2 = A; hc.l3[0].w2 = d;
-  hc.l3[0].wsrc_type = SRC_F32; hc.l3[0].ld = hc.NC3; hc.l3[0].ncols = (int)(hc.ms + hc.mt);
-  hc.l3[0].nsamples = (int)B; hc.l3[0].wsrc_stride_b = p * hc.NC3; hc.l3[0].split = (int)hc.ms;
+  hc.l3[0].wsrc_type = SRC_F32; hc.l3[0].ld = hc.NC3; hc.l3[0].ncols = (int)(hc.NC1 + hc.mt);
+  hc.l3[0].nsamples = (int)B; hc.l3[0].wsrc_stride_b = p * hc.NC3; hc.l3[0].split = hc.NC1;
   hc.p3.bf16 = bf16; hc.p3.NCB = ncb3; hc.p3.HL = 2; hc.p3.B = B; hc.p3.T = T; hc.p3.store = false;
   plan_pass(hc.p3, hc.l3, bump);
   hc.bytes = align_up(bump.off);
@@ -596,11 +596,8 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   hipError_t he = run_pass(hc.p1, hc.l1, base, stream, tr);
   if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr);
   if (he == hipSuccess)
-    he = launch_hpp_basis((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.ms, kRankTau,
-                          (double*)(base + hc.off_qd), (double*)(base + hc.off_v), W3, hc.NC3, rk, stream);
-  if (he == hipSuccess)
-    he = launch_hpp_tail(P, dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, (int)hc.mt, (int)B, (int)p, (int)hc.ms,
-                         (int)hc.mt, (const double*)(base + hc.off_qd), rk, W3, hc.NC3, stream);
+    he = launch_hpp_qr((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.mt, P,
+                       dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, base + hc.off_qr, stream);
   if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr);
   if (he == hipSuccess)
     he = launch_finish((const double2*)(base + hc.p3.off_partials), (int32_t)B, hc.p3.slots, n, accumulate, head,

@@ -18,6 +18,7 @@ namespace dpn {
 constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
+constexpr int kYsumChunk = 1024;  // elements of a Y tile per split-T reduction work group
 constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
 
 enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1 };
@@ -32,7 +33,8 @@ struct LayerRec {
   float* Yout;         // stored Y [B][w2][NC] (store mode only)
   int64_t w_stride_b;  // packed-W units between samples (0: W shared by the batch)
   int32_t w1, w2;
-  int32_t slot_base;   // first partial slot of this layer within a sample
+  int32_t slot_base;   // first partial slot of this layer within a sample (per column block, or
+                       // per column block and tile chunk when T is split)
   int32_t split;       // columns < split go to the first sum, the rest to the second
 };
 
@@ -83,17 +85,20 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStr
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s);
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s);
+// work groups of the split-T reduction per (layer, sample, column block)
+inline int ysum_chunks(int cols_per_block, int NCB) { return (cols_per_block * 16 * NCB + kYsumChunk - 1) / kYsumChunk; }
 hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, float* n, int accumulate,
                          float* head, float* tail, float* c, float C, int with_clip, hipStream_t s);
 hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s);
 
-// Hutch++: orthonormal basis of the sketch X [B][p][ldx] (first m columns)
-// into W3 [B][p][ldw] columns 0..m-1 (kept columns first, then zeros), rank
-// per sample; then P' = P - Q (Q^T P) into columns m..m+mt-1.
-hipError_t launch_hpp_basis(const float* X, int ldx, int B, int p, int m, float tau, double* Qd, double* vbuf,
-                            float* W3, int ldw, int32_t* rank, hipStream_t s);
-hipError_t launch_hpp_tail(const void* P, int ptype, int ldp, int B, int p, int m, int mt, const double* Qd,
-                           const int32_t* rank, float* W3, int ldw, hipStream_t s);
+// Hutch++: orthonormal basis Q of the sketch X [B][p][MP] (MP = 16 or 32
+// columns, zero past m_s; dropped columns give zero columns of Q) and
+// P' = P - Q (Q^T P), written as W3 [B][p][ldw] = [Q (MP columns) | P' (mt
+// columns)], rank per sample into rank [B]. `scratch` holds
+// hpp_qr_scratch_bytes(MP, B, p) bytes (256-byte aligned).
+size_t hpp_qr_scratch_bytes(int MP, int B, int p);
+hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
+                         int ldw, int32_t* rank, void* scratch, hipStream_t s);
 
 // Exact squared norms: one fp64 partial per tile into partials [B][slots].
 void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots);

@@ -463,31 +463,44 @@ __global__ void __launch_bounds__(256) k_tcontract_f32(StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-T reduction: for one (layer, sample, column block) sum the nsplit
-// partial tiles in split order (fp64), then either square and reduce into the
-// partial slot (MODE_SQ) or store Y (MODE_STORE).
+// Split-T reduction: one work group per kYsumChunk elements of the Y tile of
+// a (layer, sample, column block). Each thread sums 4 consecutive elements
+// over the nsplit partial tiles in split order (fp64), then either squares
+// and reduces into its own partial slot (MODE_SQ) or stores Y (MODE_STORE).
 // ---------------------------------------------------------------------------
 template <int MODE>
-__global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_block) {
-  const int4 it = a.items[(int64_t)blockIdx.x * a.nsplit];
+__global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_block, int ychunks) {
+  const int blk = blockIdx.x / ychunks, chunk = blockIdx.x - blk * ychunks;
+  const int4 it = a.items[(int64_t)blk * a.nsplit];
   const LayerRec* L = a.recs + it.x;
   const int i = it.y, ub = it.z;
   const int w = L->w2;
   const int u0 = ub * cols_per_block;
-  const int ucount = min(cols_per_block, w - u0);
-  const int nel = ucount * NC;
+  const int nel = min(cols_per_block, w - u0) * NC;
   const int64_t tile = (int64_t)a.B * w * NC;
   const float* Yp = L->Ypart + ((int64_t)i * w + u0) * NC;
-  double s0 = 0.0, s1 = 0.0;
+  const int e = chunk * kYsumChunk + 4 * (int)threadIdx.x;
   const int split = L->split;
-  for (int e = threadIdx.x; e < nel; e += 256) {
-    double y = 0.0;
-    for (int ts = 0; ts < a.nsplit; ++ts) y += (double)Yp[ts * tile + e];
+  double s0 = 0.0, s1 = 0.0;
+  if (e < nel) {  // nel is a multiple of 16, so all four elements are in the tile
+    double y[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int ts = 0; ts < a.nsplit; ++ts) {
+      const float4 v = ldg_f32x4(Yp + ts * tile + e);
+      y[0] += (double)v.x;
+      y[1] += (double)v.y;
+      y[2] += (double)v.z;
+      y[3] += (double)v.w;
+    }
     if (MODE == MODE_SQ) {
-      if (e % NC < split) s0 += y * y;
-      else s1 += y * y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if ((e + q) % NC < split) s0 += y[q] * y[q];
+        else s1 += y[q] * y[q];
+      }
     } else {
-      L->Yout[((int64_t)i * w + u0) * NC + e] = (float)y;
+      float* dst = L->Yout + ((int64_t)i * w + u0) * NC + e;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) stg_f32(dst + q, (float)y[q]);
     }
   }
   if (MODE == MODE_SQ) {
@@ -501,7 +514,7 @@ __global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_
     }
     __syncthreads();
     if (threadIdx.x == 0)
-      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub] =
+      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub * ychunks + chunk] =
           make_double2((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]),
                        (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]));
   }
@@ -609,11 +622,13 @@ hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct,
 
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s) {
   const int blocks = a.n_items / a.nsplit;
+  const int ychunks = ysum_chunks(cols_per_block, NCB);
   if (blocks <= 0) return hipSuccess;
+  const dim3 grid(blocks * ychunks);
   if (mode == MODE_SQ)
-    hipLaunchKernelGGL(k_ysum<MODE_SQ>, dim3(blocks), dim3(256), 0, s, a, 16 * NCB, cols_per_block);
+    hipLaunchKernelGGL(k_ysum<MODE_SQ>, grid, dim3(256), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   else
-    hipLaunchKernelGGL(k_ysum<MODE_STORE>, dim3(blocks), dim3(256), 0, s, a, 16 * NCB, cols_per_block);
+    hipLaunchKernelGGL(k_ysum<MODE_STORE>, grid, dim3(256), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   return hipGetLastError();
 }
 

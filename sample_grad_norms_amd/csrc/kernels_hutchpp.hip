@@ -8,136 +8,284 @@
 // ||A^T G Q||_F^2 is exact on span(Q) and the tail is a Hutchinson estimate
 // on the complement, ||A^T G (I - Q Q^T) P||_F^2.
 //
-// The basis is built by Gram-Schmidt with each column projected against the
-// kept basis twice, in fp64, one work group per sample. A column is kept when
-// its residual norm exceeds tau times the largest column norm of X. The kept
-// columns are written compacted, zero columns after them, into the first m_s
-// columns of the stage-1 matrix W3 = [Q | P'] of the head/tail pass; the
-// tail kernel writes P' = P - Q (Q^T P) into the next m_t columns.
+// Q is the Q factor of X with positive diagonal (unique for the kept
+// columns), by Cholesky QR in fp64, in three kernels:
+//   k_hpp_gram  : partial X^T X and X^T P over chunks of rows with fp64 MFMA
+//                 (v_mfma_f64_16x16x4), many work groups per sample;
+//   k_hpp_chol  : one wave per sample sums the partials in a fixed order and
+//                 factors X^T X = R^T R column by column in LDS (lane l fills
+//                 column l of each row of R) with a rank rule: column j is kept when its residual after
+//                 projecting out the kept columns before it (the Cholesky
+//                 diagonal) exceeds tau times the largest column norm of X;
+//                 then Ri = R^-1 on the kept columns (zero rows and columns
+//                 elsewhere), M = Q^T P = Ri^T X^T P and N = Ri M;
+//   k_hpp_apply : Q = X Ri and P' = P - Q M = P - X N with fp64 MFMA.
+// Columns keep their positions: a dropped column of X gives a zero column of
+// Q, which adds nothing to the head. W3 = [Q (MP columns) | P' (m_t)].
+// The rank rule bounds the condition number of the kept columns by about
+// 1/tau, so Q is orthonormal to about (1/tau)^2 * 2^-53 ~ 1e-6 in fp64.
 #include "device_common.h"
 #include "internal.h"
 
 namespace dpn {
 
-constexpr int kQrThreads = 256;
-constexpr int kMaxCols = 32;
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMaxTail = 32;
+constexpr int kGramRows = 256;   // rows of X per k_hpp_gram work group
+constexpr int kApplyRows = 64;   // rows of X per k_hpp_apply work group (4 waves x 16)
 
-// Sum of `cnt` per-thread values over the work group; every thread gets the
-// totals. `red` holds kQrThreads / 64 * kMaxCols doubles.
-__device__ __forceinline__ void block_sum(double* v, int cnt, double* red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int j = 0; j < cnt; ++j) {
-    const double s = wave_sum(v[j]);
-    if (lane == 0) red[wv * kMaxCols + j] = s;
-  }
-  __syncthreads();
-  for (int j = 0; j < cnt; ++j) {
-    double s = 0.0;
+__device__ __forceinline__ f64x4_t mfma_f64(double a, double b, f64x4_t c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+template <int MP>
+struct HppTiles {
+  static constexpr int TA = MP / 16;            // 16-column tiles of X
+  static constexpr int NG = TA * (TA + 1) / 2;  // Gram tiles (upper triangle)
+  static constexpr int NT = NG + 2 * TA;        // + X^T P tiles (tail columns up to 32)
+};
+
+__device__ __forceinline__ double tail_val(const void* P, int ptype, int p, int mt, int row, int t) {
+  if (row >= p || t >= mt) return 0.0;
+  if (ptype == SRC_BF16) return (double)bf16_bits_to_f32(((const uint16_t*)P)[(int64_t)row * mt + t]);
+  return (double)ldg_f32((const float*)P + (int64_t)row * mt + t);
+}
+
+// Partial tiles of X^T X (upper triangle) and X^T P for kGramRows rows:
+// part [B][nparts][NT][4][64] (the accumulator registers of each tile).
+// The contraction runs over rows: K slot l / 16 is row 4 ks + l / 16.
+template <int MP>
+__global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, int p, int mt,
+                                                  const void* __restrict__ P, int ptype, double* part) {
+  using H = HppTiles<MP>;
+  constexpr int TA = H::TA, NG = H::NG, NT = H::NT;
+  __shared__ double red[4][NT][4][64];
+  const int s = blockIdx.x, i = blockIdx.y, nparts = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const float* Xi = X + (int64_t)i * p * MP;
+  f64x4_t acc[NT];
 #pragma unroll
-    for (int w = 0; w < kQrThreads / 64; ++w) s += red[w * kMaxCols + j];
-    v[j] = s;
+  for (int t = 0; t < NT; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  constexpr int U = kGramRows / 4 / 4;  // K steps per wave, loads issued together
+  double xa[U][TA], pv[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int row = s * kGramRows + 4 * (wv * U + u) + g;
+#pragma unroll
+    for (int a = 0; a < TA; ++a) xa[u][a] = row < p ? (double)ldg_f32(Xi + (int64_t)row * MP + 16 * a + n) : 0.0;
+    pv[u][0] = tail_val(P, ptype, p, mt, row, n);
+    pv[u][1] = tail_val(P, ptype, p, mt, row, 16 + n);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int a = 0, t = 0; a < TA; ++a)
+#pragma unroll
+      for (int b = a; b < TA; ++b, ++t) acc[t] = mfma_f64(xa[u][a], xa[u][b], acc[t]);
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[NG + 2 * a + tt] = mfma_f64(xa[u][a], pv[u][tt], acc[NG + 2 * a + tt]);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wv][t][j][lane] = acc[t][j];
+  __syncthreads();
+  double* out = part + ((int64_t)i * nparts + s) * NT * 256;
+  for (int e = tid; e < NT * 256; e += 256) {
+    const int t = e >> 8, j = (e >> 6) & 3, l = e & 63;
+    out[e] = (red[0][t][j][l] + red[1][t][j][l]) + (red[2][t][j][l] + red[3][t][j][l]);
+  }
+}
+
+// One wave per sample: sum of the partial tiles, Cholesky with the rank rule,
+// Ri, M and N. Ri [B][MP][MP] and N [B][MP][32] go to global memory.
+template <int MP>
+__global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part, int nparts, float tau, double* Ri_g,
+                                                 double* N_g, int32_t* rank_out) {
+  using H = HppTiles<MP>;
+  constexpr int TA = H::TA, NG = H::NG, NT = H::NT;
+  __shared__ double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail];
+  const int i = blockIdx.x, l = threadIdx.x;
+  const double* pi = part + (int64_t)i * nparts * NT * 256;
+  // fixed-order sum; lane q, element j of a v_mfma_f64_16x16x4 result is (row q/16 + 4 j, column q % 16)
+  for (int e = l; e < NT * 256; e += 64) {
+    double v = 0.0;
+    for (int s0 = 0; s0 < nparts; s0 += 8) {  // eight loads in flight, summed in part order
+      double w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = s0 + u < nparts ? pi[(int64_t)(s0 + u) * NT * 256 + e] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += w[u];
+    }
+    const int t = e >> 8, j = (e >> 6) & 3, q = e & 63;
+    const int r = (q >> 4) + 4 * j, c = q & 15;
+    if (t < NG) {
+      int a = 0, b = 0;
+      for (int aa = 0, k = 0; aa < TA; ++aa)
+        for (int bb = aa; bb < TA; ++bb, ++k)
+          if (k == t) {
+            a = aa;
+            b = bb;
+          }
+      G[16 * a + r][16 * b + c] = v;
+      G[16 * b + c][16 * a + r] = v;
+    } else {
+      const int a = (t - NG) >> 1, tt = (t - NG) & 1;
+      XP[16 * a + r][16 * tt + c] = v;
+    }
   }
   __syncthreads();
-}
 
-// X [B][p][ldx] fp32 (first m columns valid) -> basis Qd [B][m][p] fp64
-// (scratch), vbuf [B][p] fp64 (scratch), W3 [B][p][ldw] fp32 columns 0..m-1,
-// rank [B] int32 (optional).
-__global__ void __launch_bounds__(kQrThreads) k_hpp_basis(const float* __restrict__ X, int ldx, int p, int m,
-                                                          float tau, double* Qd, double* vbuf, float* W3, int ldw,
-                                                          int32_t* rank) {
-  __shared__ double red[kQrThreads / 64 * kMaxCols];
-  const int i = blockIdx.x;
-  const float* Xi = X + (int64_t)i * p * ldx;
-  double* Q = Qd + (int64_t)i * m * p;
-  double* v = vbuf + (int64_t)i * p;
-  float* Wi = W3 + (int64_t)i * p * ldw;
-
-  // largest column norm of X
-  double nrm[kMaxCols];
-  for (int j = 0; j < m; ++j) nrm[j] = 0.0;
-  for (int r = threadIdx.x; r < p; r += kQrThreads)
-    for (int j = 0; j < m; ++j) {
-      const double x = (double)Xi[(int64_t)r * ldx + j];
-      nrm[j] += x * x;
-    }
-  block_sum(nrm, m, red);
-  double scale = 0.0;
-  for (int j = 0; j < m; ++j) scale = fmax(scale, sqrt(nrm[j]));
-
-  int kept = 0;
-  double dots[kMaxCols];
-  for (int j = 0; j < m; ++j) {
-    for (int r = threadIdx.x; r < p; r += kQrThreads) v[r] = (double)Xi[(int64_t)r * ldx + j];
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int q = 0; q < kept; ++q) dots[q] = 0.0;
-      for (int r = threadIdx.x; r < p; r += kQrThreads) {
-        const double x = v[r];
-        for (int q = 0; q < kept; ++q) dots[q] += Q[(int64_t)q * p + r] * x;
-      }
-      block_sum(dots, kept, red);
-      for (int r = threadIdx.x; r < p; r += kQrThreads) {
-        double x = v[r];
-        for (int q = 0; q < kept; ++q) x -= dots[q] * Q[(int64_t)q * p + r];
-        v[r] = x;
+  // Cholesky, column by column: every lane forms the residual of column j
+  // (uniform LDS reads), then lane l > j fills R[j][l].
+  for (int e = l; e < MP * MP; e += 64) {
+    (&R[0][0])[e] = 0.0;
+    (&Ri[0][0])[e] = 0.0;
+  }
+  double dmax = 0.0;
+  for (int j = 0; j < MP; ++j) dmax = fmax(dmax, G[j][j]);
+  const double scale = sqrt(fmax(dmax, 0.0));
+  __syncthreads();
+  uint32_t keep = 0;
+  for (int j = 0; j < MP; ++j) {
+    double sj = G[j][j];
+    for (int c = 0; c < j; ++c)
+      if ((keep >> c) & 1u) sj -= R[c][j] * R[c][j];
+    const double nj = sqrt(fmax(sj, 0.0));
+    if (nj > (double)tau * scale && nj > 0.0) {
+      keep |= 1u << j;
+      if (l == j) R[j][j] = nj;
+      if (l > j && l < MP) {
+        double t = G[j][l];
+        for (int c = 0; c < j; ++c)
+          if ((keep >> c) & 1u) t -= R[c][j] * R[c][l];
+        R[j][l] = t / nj;
       }
     }
-    double nv = 0.0;
-    for (int r = threadIdx.x; r < p; r += kQrThreads) nv += v[r] * v[r];
-    block_sum(&nv, 1, red);
-    nv = sqrt(nv);
-    if (nv > (double)tau * scale && nv > 0.0) {
-      const double inv = 1.0 / nv;
-      for (int r = threadIdx.x; r < p; r += kQrThreads) Q[(int64_t)kept * p + r] = v[r] * inv;
-      ++kept;
+    __syncthreads();
+  }
+  // Ri: lane c computes column c by back substitution (zero off the kept columns)
+  if (l < MP && ((keep >> l) & 1u)) {
+    const int c = l;
+    Ri[c][c] = 1.0 / R[c][c];
+    for (int r = c - 1; r >= 0; --r) {
+      if (!((keep >> r) & 1u)) continue;
+      double t = 0.0;
+      for (int q = r + 1; q <= c; ++q)
+        if ((keep >> q) & 1u) t += R[r][q] * Ri[q][c];
+      Ri[r][c] = -t / R[r][r];
     }
-    // every thread reads v and Q of its own rows only; the block_sum barriers
-    // order the next column's reads after these writes
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < p; r += kQrThreads)
-    for (int j = 0; j < m; ++j) Wi[(int64_t)r * ldw + j] = j < kept ? (float)Q[(int64_t)j * p + r] : 0.f;
-  if (rank && threadIdx.x == 0) rank[i] = kept;
+  double* Rig = Ri_g + (int64_t)i * MP * MP;
+  for (int e = l; e < MP * MP; e += 64) Rig[e] = (&Ri[0][0])[e];
+  // M[c][t] = sum_a Ri[a][c] XP[a][t]
+  for (int e = l; e < MP * kMaxTail; e += 64) {
+    const int c = e / kMaxTail, t = e % kMaxTail;
+    double v = 0.0;
+    for (int a = 0; a <= c; ++a) v += Ri[a][c] * XP[a][t];
+    M[c][t] = v;
+  }
+  __syncthreads();
+  // N[a][t] = sum_c Ri[a][c] M[c][t]
+  double* Ng = N_g + (int64_t)i * MP * kMaxTail;
+  for (int e = l; e < MP * kMaxTail; e += 64) {
+    const int a = e / kMaxTail, t = e % kMaxTail;
+    double v = 0.0;
+    for (int c = a; c < MP; ++c) v += Ri[a][c] * M[c][t];
+    Ng[e] = v;
+  }
+  if (l == 0 && rank_out) rank_out[i] = __popc(keep);
 }
 
-// Tail column tcol of sample i: P'[:, tcol] = P[:, tcol] - Q (Q^T P[:, tcol]),
-// written to W3 column m + tcol. Grid (B, m_t).
-__global__ void __launch_bounds__(kQrThreads) k_hpp_tail(const void* __restrict__ P, int ptype, int ldp, int p,
-                                                         int m, const double* __restrict__ Qd,
-                                                         const int32_t* __restrict__ rank_in, float* W3, int ldw) {
-  __shared__ double red[kQrThreads / 64 * kMaxCols];
-  const int i = blockIdx.x, tcol = blockIdx.y;
-  const double* Q = Qd + (int64_t)i * m * p;
+// Q = X Ri and P' = P - X N for kApplyRows rows (16 per wave); K slot l / 16
+// is column 4 ks + l / 16 of X.
+template <int MP>
+__global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, int p, int mt,
+                                                   const void* __restrict__ P, int ptype,
+                                                   const double* __restrict__ Ri_g, const double* __restrict__ N_g,
+                                                   float* W3, int ldw) {
+  constexpr int TA = MP / 16;
+  __shared__ double Ri[MP][MP], N[MP][kMaxTail];
+  const int i = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  for (int e = tid; e < MP * MP; e += 256) (&Ri[0][0])[e] = Ri_g[(int64_t)i * MP * MP + e];
+  for (int e = tid; e < MP * kMaxTail; e += 256) (&N[0][0])[e] = N_g[(int64_t)i * MP * kMaxTail + e];
+  const float* Xi = X + (int64_t)i * p * MP;
   float* Wi = W3 + (int64_t)i * p * ldw;
-  const int kept = rank_in[i];
-  auto pval = [&](int r) -> double {
-    if (ptype == SRC_BF16) return (double)bf16_bits_to_f32(((const uint16_t*)P)[(int64_t)r * ldp + tcol]);
-    return (double)((const float*)P)[(int64_t)r * ldp + tcol];
-  };
-  double dots[kMaxCols];
-  for (int q = 0; q < kept; ++q) dots[q] = 0.0;
-  for (int r = threadIdx.x; r < p; r += kQrThreads) {
-    const double x = pval(r);
-    for (int q = 0; q < kept; ++q) dots[q] += Q[(int64_t)q * p + r] * x;
+  const int r0 = blockIdx.x * kApplyRows + 16 * wv;
+  const int arow = r0 + n;
+  double xa[MP / 4], pr[4][2];
+#pragma unroll
+  for (int ks = 0; ks < MP / 4; ++ks) xa[ks] = arow < p ? (double)ldg_f32(Xi + (int64_t)arow * MP + 4 * ks + g) : 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = r0 + g + 4 * j;
+    pr[j][0] = tail_val(P, ptype, p, mt, row, n);
+    pr[j][1] = tail_val(P, ptype, p, mt, row, 16 + n);
   }
-  block_sum(dots, kept, red);
-  for (int r = threadIdx.x; r < p; r += kQrThreads) {
-    double x = pval(r);
-    for (int q = 0; q < kept; ++q) x -= dots[q] * Q[(int64_t)q * p + r];
-    Wi[(int64_t)r * ldw + m + tcol] = (float)x;
+  __syncthreads();
+  f64x4_t q[TA], pn[2];
+#pragma unroll
+  for (int t = 0; t < TA; ++t) q[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  pn[0] = pn[1] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < MP / 4; ++ks) {
+    const int col = 4 * ks + g;
+#pragma unroll
+    for (int t = 0; t < TA; ++t) q[t] = mfma_f64(xa[ks], Ri[col][16 * t + n], q[t]);
+    pn[0] = mfma_f64(xa[ks], N[col][n], pn[0]);
+    pn[1] = mfma_f64(xa[ks], N[col][16 + n], pn[1]);
+  }
+  // lane l, element j of a v_mfma_f64_16x16x4 result: row l/16 + 4 j, column l % 16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = r0 + g + 4 * j;
+    if (row >= p) continue;
+    float* wr = Wi + (int64_t)row * ldw;
+#pragma unroll
+    for (int t = 0; t < TA; ++t) stg_f32(wr + 16 * t + n, (float)q[t][j]);
+    if (n < mt) stg_f32(wr + MP + n, (float)(pr[j][0] - pn[0][j]));
+    if (16 + n < mt) stg_f32(wr + MP + 16 + n, (float)(pr[j][1] - pn[1][j]));
   }
 }
 
-hipError_t launch_hpp_basis(const float* X, int ldx, int B, int p, int m, float tau, double* Qd, double* vbuf,
-                            float* W3, int ldw, int32_t* rank, hipStream_t s) {
-  hipLaunchKernelGGL(k_hpp_basis, dim3(B), dim3(kQrThreads), 0, s, X, ldx, p, m, tau, Qd, vbuf, W3, ldw, rank);
+size_t hpp_qr_scratch_bytes(int MP, int B, int p) {
+  const int nparts = (p + kGramRows - 1) / kGramRows;
+  const int NT = MP == 16 ? HppTiles<16>::NT : HppTiles<32>::NT;
+  const size_t part = (size_t)B * nparts * NT * 256 * 8;
+  const size_t ri = (size_t)B * MP * MP * 8, nn = (size_t)B * MP * kMaxTail * 8;
+  return ((part + 255) / 256 + (ri + 255) / 256 + (nn + 255) / 256) * 256;
+}
+
+template <int MP>
+static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
+                         int ldw, int32_t* rank, char* scratch, hipStream_t s) {
+  const int nparts = (p + kGramRows - 1) / kGramRows;
+  constexpr int NT = HppTiles<MP>::NT;
+  double* part = (double*)scratch;
+  double* Ri = (double*)(scratch + ((size_t)B * nparts * NT * 256 * 8 + 255) / 256 * 256);
+  double* N = (double*)((char*)Ri + ((size_t)B * MP * MP * 8 + 255) / 256 * 256);
+  hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hpp_chol<MP>, dim3(B), dim3(64), 0, s, part, nparts, tau, Ri, N, rank);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hpp_apply<MP>, dim3((p + kApplyRows - 1) / kApplyRows, B), dim3(256), 0, s, X, p, mt, P,
+                     ptype, Ri, N, W3, ldw);
   return hipGetLastError();
 }
 
-hipError_t launch_hpp_tail(const void* P, int ptype, int ldp, int B, int p, int m, int mt, const double* Qd,
-                           const int32_t* rank, float* W3, int ldw, hipStream_t s) {
-  hipLaunchKernelGGL(k_hpp_tail, dim3(B, mt), dim3(kQrThreads), 0, s, P, ptype, ldp, p, m, Qd, rank, W3, ldw);
-  return hipGetLastError();
+hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
+                         int ldw, int32_t* rank, void* scratch, hipStream_t s) {
+  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, s);
+  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dpn
