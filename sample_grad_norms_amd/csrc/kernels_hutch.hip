@@ -117,6 +117,12 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
 // over the LDS banks. After the last stage lane l of wave w holds rows
 // slot_row(l / 16, s) of chunk w, so the hi/lo bf16 B-operand fragments of
 // stage 2 are written straight from the accumulators.
+// Each work group starts its pass over the columns at its own stage and wraps
+// around: when every group reads the same column offset of rows whose length
+// is a large power of two, the concurrent reads fall on few HBM channels.
+// Groups are dealt to the XCDs round robin, so the eight neighbours of a
+// group (one per XCD) share a start and the groups that share an XCD get
+// starts 41 stages apart (modulo the stage count).
 // V layout: [B][Tpad/32][NCB][2][64] uint4.
 // ---------------------------------------------------------------------------
 constexpr int kK1Cols = 64;                          // columns of X1 per stage (one 128-byte line)
@@ -159,6 +165,7 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
   const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
   const int nst = (w + kK1Cols - 1) / kK1Cols;
+  const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nst);  // first column stage of this group
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
   // X1 source of this lane: instruction j of wave wv fills LDS rows
@@ -171,7 +178,8 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
   auto dma = [&](int st) {
     if (st >= nst) return;
     const uint32_t buf = lds_base + (uint32_t)((st % kK1Bufs) * kStage);
-    int col = st * kK1Cols + gunit * 8;
+    const int cst = st + rot < nst ? st + rot : st + rot - nst;  // column stage read at step st
+    int col = cst * kK1Cols + gunit * 8;
     col = col < w ? col : w - 8;
 #pragma unroll
     for (int j = 0; j < kK1XDma; ++j) {
@@ -182,7 +190,7 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int m0 = 0; m0 < (kWBlocks + 3) / 4; ++m0) {
       const int m = 4 * m0 + wv;
-      if (m < kWBlocks) dma16(Wp + ((int64_t)st * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
+      if (m < kWBlocks) dma16(Wp + ((int64_t)cst * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
     }
   };
 
