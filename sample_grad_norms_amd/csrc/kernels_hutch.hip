@@ -358,13 +358,36 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
 
 // ---------------------------------------------------------------------------
 // Stage 2, bf16: Y = X2^T V over the chunks of one T split, for 512 columns
-// of X2 (4 waves x 128). Per 32-row chunk a lane loads 8 rows (slot_row) of
-// its 8 consecutive columns, transposes the 8 x 8 block in registers so the
-// contraction index runs along the MFMA K slots, and multiplies it against
-// the hi and lo fragments of V; the next chunk's loads are in flight meanwhile.
+// of X2 (4 waves x 128).
+//
+// Each 32-row chunk of X2 (32 rows x 1 KB) and its V fragments are streamed
+// into LDS with direct global-to-LDS loads, as in stage 1 (wave w loads rows
+// 8w..8w+7 of the chunk and one or two 1 KB V blocks), with three chunks in
+// flight while one is multiplied. A lane then reads 8 rows (slot_row) of its
+// 8 consecutive columns from LDS, transposes the 8 x 8 block in registers so
+// the contraction index runs along the MFMA K slots, and multiplies it
+// against the hi and lo fragments of V. Rows past T and columns past w load
+// the last valid row / column and are zeroed after the LDS read.
 // ---------------------------------------------------------------------------
+constexpr int kK2Rows = 32;                              // rows of X2 per stage (one MFMA K step)
+constexpr int kK2XBytes = kK2Rows * kColsK2Bf16 * 2;     // X2 bytes per stage (32 KB)
+
+// s_waitcnt vmcnt(after * P) for after in 0..2.
+template <int P>
+__device__ __forceinline__ void wait_after(int after) {
+  if (after >= 2) DPN_WAIT_VMCNT(2 * P);
+  else if (after == 1) DPN_WAIT_VMCNT(P);
+  else DPN_WAIT_VMCNT(0);
+}
+
 template <int NCB, bool DIRECT>
-__global__ void __launch_bounds__(256, 2) k_tcontract_bf16(StageArgs a) {
+__global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
+  constexpr int kVBlocks = 2 * NCB;                      // 1 KB V fragment blocks per chunk
+  constexpr int kStage = kK2XBytes + kVBlocks * 1024;
+  constexpr int kBufs = NCB <= 2 ? 4 : 3;                // LDS ring (stages in flight: kBufs - 1)
+  constexpr int kXDma = kK2Rows / 4;                     // 1 KB X2 rows per wave per stage
+  constexpr int kP = kXDma + kVBlocks / 4;               // loads every wave issues per stage (at least)
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
   const int4 it = a.items[xcd_item(blockIdx.x, (uint32_t)a.n_items)];
   const LayerRec* L = a.recs + it.x;
   const int i = it.y, ub = it.z, ts = it.w;
@@ -373,10 +396,30 @@ __global__ void __launch_bounds__(256, 2) k_tcontract_bf16(StageArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int wave_u0 = ub * kColsK2Bf16 + wv * 128;
   const bool uok = wave_u0 + 8 * n < w;
-  const uint16_t* X = (const uint16_t*)L->X2 + (int64_t)i * T * w + wave_u0 + 8 * n;
+  const int dcol = min(ub * kColsK2Bf16 + 8 * lane, w - 8);  // this lane's 16 bytes of each loaded row
+  const uint16_t* X = (const uint16_t*)L->X2 + (int64_t)i * T * w + dcol;
   const uint4* V = (const uint4*)L->V + (int64_t)i * (a.Tpad / 32) * (NCB * 2 * 64) + lane;
   const int nch = (T + 31) >> 5;
   const int c0 = (int)((int64_t)ts * nch / a.nsplit), c1 = (int)((int64_t)(ts + 1) * nch / a.nsplit);
+  const int ncs = c1 - c0;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+
+  auto dma = [&](int st) {
+    if (st >= ncs) return;
+    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage);
+    const int c = c0 + st;
+#pragma unroll
+    for (int j = 0; j < kXDma; ++j) {
+      int t = kK2Rows * c + kXDma * wv + j;
+      t = t < T ? t : T - 1;
+      dma16_stream(X + (int64_t)t * w, buf + (uint32_t)((kXDma * wv + j) * 1024));
+    }
+#pragma unroll
+    for (int m0 = 0; m0 < (kVBlocks + 3) / 4; ++m0) {
+      const int m = 4 * m0 + wv;
+      if (m < kVBlocks) dma16(V + ((int64_t)c * kVBlocks + m) * 64, buf + (uint32_t)(kK2XBytes + m * 1024));
+    }
+  };
 
   f32x4_t acc[8][NCB];
 #pragma unroll
@@ -385,42 +428,37 @@ __global__ void __launch_bounds__(256, 2) k_tcontract_bf16(StageArgs a) {
     for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint4 z = make_uint4(0, 0, 0, 0);
-  auto load = [&](int c, uint4 (&raw)[8], uint4 (&bv)[NCB][2]) {
-    const bool cok = c < c1;
+#pragma unroll
+  for (int st = 0; st < kBufs - 1; ++st) dma(st);
+  for (int st = 0; st < ncs; ++st) {
+    // this wave's loads of stage st have landed once at most its loads of
+    // the later stages are outstanding; the barrier publishes every wave's
+    // loads and frees the buffer of stage st - 1
+    wait_after<kP>(min(kBufs - 2, ncs - 1 - st));
+    block_barrier();
+    dma(st + kBufs - 1);
+    const unsigned char* buf = lds + (st % kBufs) * kStage;
+    const int t0 = kK2Rows * (c0 + st);
+    uint4 raw[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int t = 32 * c + slot_row(g, s);
-      raw[s] = (cok && uok && t < T) ? ldg16_stream(X + (int64_t)t * w) : z;
+      const int r = slot_row(g, s);
+      const uint4 x = *(const uint4*)(buf + r * 1024 + wv * 256 + n * 16);
+      raw[s] = (uok && t0 + r < T) ? x : z;
     }
+    uint4 bv[NCB][2];
 #pragma unroll
     for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bv[jb][h] = cok ? ldg16(V + ((int64_t)(c * NCB + jb) * 2 + h) * 64) : z;
-  };
-
-  if (wave_u0 < w) {
-    uint4 raw[8], bv[NCB][2];
-    load(c0, raw, bv);
-    for (int c = c0; c < c1; ++c) {
-      uint4 rawn[8], bvn[NCB][2];
-      load(c + 1, rawn, bvn);
-      uint4 op[8];
-      transpose8x8_bf16(raw, op);
+      for (int h = 0; h < 2; ++h) bv[jb][h] = *(const uint4*)(buf + kK2XBytes + (jb * 2 + h) * 1024 + lane * 16);
+    uint4 op[8];
+    transpose8x8_bf16(raw, op);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int jb = 0; jb < NCB; ++jb) {
-          acc[e][jb] = mfma_bf16(op[e], bv[jb][0], acc[e][jb]);
-          acc[e][jb] = mfma_bf16(op[e], bv[jb][1], acc[e][jb]);
-        }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) raw[s] = rawn[s];
-#pragma unroll
-      for (int jb = 0; jb < NCB; ++jb) {
-        bv[jb][0] = bvn[jb][0];
-        bv[jb][1] = bvn[jb][1];
-      }
-    }
+        for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = mfma_bf16(op[e], bv[jb][h], acc[e][jb]);
   }
   tcontract_epilogue<NCB, 8, DIRECT>(a, L, acc, i, ub, ts, wave_u0, 8, lane, wv);
 }
