@@ -215,7 +215,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
       P.k2_begin = pl.k2_begin[l];
       P.n2 = pl.n2[l];
       P.ubs = pl.ubs[l];
-      units += P.n_pack + P.n1 + P.n2 + 1;
+      units += (P.n_pack + P.n1 + P.n2 + 1 + 255) / 256 * 256;  // next layer starts a work group
     }
     a.nlayers = cn;
     a.total_units = units;

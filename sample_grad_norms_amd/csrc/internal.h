@@ -47,7 +47,7 @@ struct PrepLayer {
   int32_t ld, ncols;       // source row stride and valid columns (< NC pads with zeros)
   int32_t nsamples;        // 1 (shared W) or B
   int32_t layer;           // index of this layer in the record table
-  int32_t unit_begin;      // first prepare unit of this layer within the launch
+  int32_t unit_begin;      // first prepare unit of this layer within the launch (a multiple of 256)
   int32_t n_pack;          // packing units
   int32_t k1_begin, n1;    // stage-1 items: global range and count
   int32_t k2_begin, n2;    // stage-2 items: global range and count

@@ -22,6 +22,8 @@ namespace dpn {
 // ---------------------------------------------------------------------------
 // Prepare: one thread per unit. Units of a layer, in order: packed-W units,
 // stage-1 item entries, stage-2 item entries, and one unit for the record.
+// Each layer's units start on a work-group boundary, so a work group finds
+// its layer with a uniform search (scalar loads from the argument table).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float load_src(const void* p, int64_t idx, int type) {
   if (type == SRC_BF16) return bf16_bits_to_f32(((const uint16_t*)p)[idx]);
@@ -29,12 +31,12 @@ __device__ __forceinline__ float load_src(const void* p, int64_t idx, int type) 
 }
 
 __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
-  const int unit = blockIdx.x * 256 + threadIdx.x;
-  if (unit >= a.total_units) return;
+  const int first = blockIdx.x * 256;
   int l = 0;
-  while (l + 1 < a.nlayers && unit >= a.L[l + 1].unit_begin) ++l;
+  while (l + 1 < a.nlayers && first >= a.L[l + 1].unit_begin) ++l;
   const PrepLayer& P = a.L[l];
-  int r = unit - P.unit_begin;
+  int r = first + threadIdx.x - P.unit_begin;
+  if (r >= P.n_pack + P.n1 + P.n2 + 1) return;  // padding up to the next layer's first work group
   const int NCB = a.NCB, NC = 16 * NCB;
 
   if (r < P.n_pack) {
