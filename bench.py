@@ -93,6 +93,69 @@ def rotated(make, copies):
     return [make(r) for r in range(copies)]
 
 
+def hbm_calibration(dev):
+    """The device's memory clock and bus width (HIP device attributes 60 and
+    59: hipDeviceAttributeMemoryClockRate in kHz, hipDeviceAttributeMemoryBusWidth
+    in bits) with the double-data-rate peak they imply, and the rate of a
+    read-only stream over 16 GiB with the stage kernels' load path."""
+    import ctypes
+    import torch
+    import sample_grad_norms_amd as dp
+    out = {"spec_gbs": HBM_PEAK_GBS}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        clk, bus = ctypes.c_int(0), ctypes.c_int(0)
+        idx = dev.index or 0
+        if hip.hipDeviceGetAttribute(ctypes.byref(clk), 60, idx) == 0 and \
+                hip.hipDeviceGetAttribute(ctypes.byref(bus), 59, idx) == 0:
+            out["memory_clock_khz"] = clk.value
+            out["bus_width_bits"] = bus.value
+            out["ddr_formula_gbs"] = 2.0 * clk.value * 1e3 * bus.value / 8 / 1e9
+    except OSError:
+        pass
+    buf = torch.empty(16 << 30, dtype=torch.uint8, device=dev)
+    ms = timed(lambda: dp.read_probe(buf), 5, 2)
+    out["read_probe_16GiB_gbs"] = buf.numel() / (ms * 1e-3) / 1e9
+    out["note"] = ("percentages of peak in this record use spec_gbs; ddr_formula_gbs (2 x memory clock x bus "
+                   "width / 8 from the device attributes) counts two transfers per reported clock, which is "
+                   "below what HBM3E delivers here (the read probe exceeds it)")
+    del buf
+    return out
+
+
+def shared_input_stack(args):
+    """The Llama-3.2-1B-shaped stack with inputs shared as in the real model
+    (q, k, v read one activation tensor, gate and up another): projections on
+    one input share one pass over it."""
+    import torch
+    import sample_grad_norms_amd as dp
+    import workloads
+    dev = torch.device("cuda:0")
+    B, T, k = 4, 4096, 32
+    layers = workloads.shared_input_stack(device=dev, B=B, T=T, k=k)
+    ws = torch.empty(dp.hutch_grouped_workspace(layers, torch.bfloat16, B, T, k), dtype=torch.uint8, device=dev)
+    n = torch.empty(B, dtype=torch.float32, device=dev)
+    c = torch.empty(B, dtype=torch.float32, device=dev)
+
+    def step(timer=None):
+        dp.hutch_grouped(layers, out=n, C_clip=1.0, clip_out=c, workspace=ws, timer=timer)
+    ms = timed(step, args.steps, args.warmup)
+    timer = dp.KernelTimer(64)
+    per_kind = {}
+    for _ in range(3):
+        step(timer)
+        for kind, t in timer.last():
+            per_kind[kind] = per_kind.get(kind, 0.0) + t / 3
+    inputs = {A.data_ptr(): A for (A, _, _) in layers}
+    bytes_A = sum(A.numel() * A.element_size() for A in inputs.values())
+    bytes_GP = sum(G.numel() * G.element_size() + P.numel() * P.element_size() for (_, G, P) in layers)
+    out = {"ms_per_step": ms, "samples_tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": bytes_A + bytes_GP,
+           "hbm_gbs": (bytes_A + bytes_GP) / (ms * 1e-3) / 1e9, "kernel_ms": per_kind,
+           "tcontract_gbs": bytes_A / (per_kind["tcontract"] * 1e-3) / 1e9}
+    del layers, ws
+    return out
+
+
 def extras(args):
     """Other workloads: single-layer Hutchinson, Hutch++ and the exact
     comparator, each timed the same way."""
@@ -262,7 +325,9 @@ def main():
         "clip_fraction": float((c < 1.0).float().mean().item()),
     }
     if not args.no_extras:
-        rec["extras"] = extras(args)
+        rec["extras"] = {"hbm_calibration": hbm_calibration(dev),
+                         "llama_shared_inputs_B4_T4096_k32": shared_input_stack(args)}
+        rec["extras"].update(extras(args))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(layers, B, T, max(1, min(16, args.cpu_layers)))
     print(json.dumps(rec), flush=True)

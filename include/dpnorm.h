@@ -116,6 +116,13 @@ const char* dpnorm_status_string(int status);
  * columns. Returns DPNORM_ERR_SIZE when k < 3 (no tail) or k > 96. */
 dpnorm_status dpnorm_hutchpp_split(int64_t k, int64_t* m_s, int64_t* m_t);
 
+/* Calibration (not part of the estimator): reads `bytes` (a positive
+ * multiple of 16384, at most 2^44) from the device buffer `buf` (16-byte
+ * aligned) once, with the direct global-to-LDS loads the stage kernels use,
+ * and discards the data. Timing it gives the read rate that load path
+ * reaches on this device. Errors: ERR_NULL, ERR_SIZE, ERR_ALIGN, ERR_HIP. */
+dpnorm_status dpnorm_read_probe(const void* buf, int64_t bytes, hipStream_t stream);
+
 /* ---- workspace queries (host only; no device work) ---- */
 dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p,
                                      int64_t k, size_t* bytes);
@@ -141,7 +148,16 @@ dpnorm_status dpnorm_hutch(const void* A, const void* G, const void* P, dpnorm_d
  * Same semantics as L dpnorm_hutch calls with accumulate = 1 after the first,
  * in fewer launches. `layers` is a host array of L >= 1 descriptors with
  * device pointers. If c is not NULL, c[i] = min(C / sqrt(n[i]), 1) is also
- * written from the final n (then C must be finite and > 0; c may equal n). */
+ * written from the final n (then C must be finite and > 0; c may equal n).
+ * Layers whose descriptors carry the same A pointer and the same d (in a
+ * transformer block: q, k and v read one input, and so do gate and up) share
+ * one pass over A: sum_m ||A^T (G_m P_m)||_F^2 = ||A^T [G_1 P_1 | G_2 P_2 ...]||_F^2,
+ * so A is read once for the group (up to 96 projected columns per pass). The
+ * result is the same sum, up to rounding order.
+ * Workspace: dpnorm_hutch_grouped_workspace given the same descriptors
+ * (pointers included) sizes this plan; given NULL A pointers it sizes the
+ * plan without sharing, and a call with such a workspace runs without
+ * sharing when the shared plan would need more. */
 dpnorm_status dpnorm_hutch_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
                                    int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
                                    void* ws, size_t ws_bytes, hipStream_t stream);

@@ -138,11 +138,17 @@ def hutch_workspace(dtype: torch.dtype, B: int, T: int, d: int, p: int, k: int) 
 
 
 def hutch_grouped_workspace(layers, dtype: torch.dtype, B: int, T: int, k: int) -> int:
-    """Workspace bytes of dpnorm_hutch_grouped for (d, p) pairs or layer tensors."""
+    """Workspace bytes of dpnorm_hutch_grouped for layer tensors or (d, p) pairs.
+
+    Given the (A, G, P) tensors, the size is that of the call's own plan, in
+    which layers sharing one A tensor share one pass over it. Given (d, p)
+    pairs, it is the size without that sharing; a call with such a workspace
+    still succeeds and then streams each A separately if it must.
+    """
     arr = (_lib.Layer * len(layers))()
     for j, y in enumerate(layers):
         if isinstance(y[0], torch.Tensor):
-            arr[j] = _lib.Layer(None, None, None, y[0].shape[2], y[1].shape[2])
+            arr[j] = _lib.Layer(y[0].data_ptr(), y[1].data_ptr(), y[2].data_ptr(), y[0].shape[2], y[1].shape[2])
         else:
             arr[j] = _lib.Layer(None, None, None, int(y[0]), int(y[1]))
     nbytes = C.c_size_t(0)
@@ -172,10 +178,19 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     c = None
     if C_clip is not None:
         c = _out(clip_out, B, device, False, "clip_out") if clip_out is not None else torch.empty_like(n)
-    ws, wsp = _given_workspace(workspace, nbytes.value, device)
+    if workspace is None:
+        ws, wsp = _workspace(nbytes.value, device)
+        ws_bytes = nbytes.value
+    else:
+        # the library decides whether a smaller workspace still fits a plan
+        # without shared-input passes (see hutch_grouped_workspace)
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a GPU tensor")
+        ws, wsp = workspace, workspace.data_ptr()
+        ws_bytes = workspace.numel() * workspace.element_size()
     args = (arr, len(layers), _code(dtype), B, T, k, n.data_ptr(), int(accumulate),
             c.data_ptr() if c is not None else None, float(C_clip) if C_clip is not None else 1.0,
-            wsp, nbytes.value, _stream(device))
+            wsp, ws_bytes, _stream(device))
     if timer is None:
         _check(L.dpnorm_hutch_grouped(*args), "dpnorm_hutch_grouped")
     else:
@@ -183,6 +198,17 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
         _check(L.dpnorm_hutch_grouped_traced(*args, C.byref(tr)), "dpnorm_hutch_grouped_traced")
         timer._record(tr)
     return (n, c) if c is not None else n
+
+
+def read_probe(buf: torch.Tensor) -> None:
+    """Calibration: stream the whole of ``buf`` (a contiguous GPU tensor whose
+    size is a multiple of 16384 bytes) once with the stage kernels' direct
+    global-to-LDS loads (dpnorm_read_probe); time it to get that path's read
+    rate."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _check(lib().dpnorm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), _stream(buf.device)),
+           "dpnorm_read_probe")
 
 
 _ROUTES = {"auto": _lib.EXACT_AUTO, "explicit": _lib.EXACT_EXPLICIT, "gram": _lib.EXACT_GRAM}

@@ -22,6 +22,7 @@ SOURCES = [
     "kernels_hutch.hip",
     "kernels_hutchpp.hip",
     "kernels_exact.hip",
+    "kernels_calib.hip",
     "dpnorm.cpp",
 ]
 

@@ -55,15 +55,30 @@ struct PassLayer {
   float* Yout = nullptr;        // store mode destination [B][w2][NC]
 };
 
+// Layers that read the same X2 (same pointer and width) form one stage-2
+// group: their V blocks sit side by side in one V, so X2 is streamed once
+// for all of them and the squared norm of the wide Y is the sum of theirs.
+struct PassGroup {
+  std::vector<int> members;     // layer indices, in call order
+  int ncb = 0;                  // column blocks of the group's V (members x NCB)
+  int ubs = 0;                  // stage-2 column blocks of X2 per sample
+  int k2_begin = 0, n2 = 0;     // stage-2 items
+  int slot_base = 0;
+  size_t off_V = 0, off_Yp = 0;
+};
+
 struct PassPlan {
   bool bf16 = true;
   int NCB = 2, HL = 1;
   int64_t B = 0, T = 0, Tpad = 0;
   int nch = 0, nsplit = 1, cols2 = kColsK2Bf16, rbs = 0;
   bool store = false;
+  bool fuse = false;            // group layers that share X2
   size_t off_recs = 0, off_items1 = 0, off_items2 = 0, off_partials = 0;
-  std::vector<size_t> off_W, off_V, off_Yp;
-  std::vector<int> k1_begin, n1, k2_begin, n2, ubs, slot_base, n_pack;
+  std::vector<size_t> off_W;
+  std::vector<int> k1_begin, n1, n_pack, group_of, jb0;  // per layer
+  std::vector<PassGroup> groups;
+  std::vector<int> class_ncb, class_begin, class_end;    // stage-2 item ranges, one per group width
   int64_t total1 = 0, total2 = 0;
   int slots = 0;
   bool direct() const { return !store && nsplit == 1; }
@@ -72,9 +87,43 @@ struct PassPlan {
 
 int ncb_of(int64_t ncols) { return ncols <= 16 ? 1 : (ncols <= 32 ? 2 : 4); }
 
+// Group widths (in 16-column blocks) that stage 2 is built for.
+bool ncb_supported(int ncb) { return ncb == 1 || ncb == 2 || ncb == 3 || ncb == 4 || ncb == 6; }
+
 size_t packed_units(const PassPlan& pl, int64_t rows) {
   if (pl.bf16) return (size_t)((rows + 63) / 64 * 2) * pl.NCB * pl.HL * 64;  // uint4 units, even K steps
   return (size_t)((rows + 15) / 16 * 16) * 16 * pl.NCB;                   // floats
+}
+
+// Stage-2 groups: with pl.fuse, layers with the same (X2, w2) are grouped in
+// call order, each group as wide as the supported widths allow; otherwise
+// every layer is its own group.
+void form_groups(PassPlan& pl, const std::vector<PassLayer>& L) {
+  const int nl = (int)L.size();
+  pl.groups.clear();
+  std::vector<int> done(nl, 0);
+  for (int l = 0; l < nl; ++l) {
+    if (done[l]) continue;
+    std::vector<int> same{l};
+    done[l] = 1;
+    if (pl.fuse && L[l].X2) {
+      for (int m = l + 1; m < nl; ++m)
+        if (!done[m] && L[m].X2 == L[l].X2 && L[m].w2 == L[l].w2) {
+          same.push_back(m);
+          done[m] = 1;
+        }
+    }
+    size_t at = 0;
+    while (at < same.size()) {
+      int take = (int)std::min<size_t>(same.size() - at, 6 / pl.NCB > 0 ? 6 / pl.NCB : 1);
+      while (take > 1 && !ncb_supported(take * pl.NCB)) --take;
+      PassGroup g;
+      g.members.assign(same.begin() + at, same.begin() + at + take);
+      g.ncb = take * pl.NCB;
+      pl.groups.push_back(g);
+      at += take;
+    }
+  }
 }
 
 // Lay out one pass over `L` in the workspace. Only sizes are used.
@@ -84,12 +133,19 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   pl.nch = (int)((pl.T + 31) / 32);
   pl.rbs = (int)(pl.Tpad / kRowsK1);
   pl.cols2 = pl.bf16 ? kColsK2Bf16 : kColsK2F32;
-  const int NC = 16 * pl.NCB;
-  pl.ubs.assign(nl, 0);
+  form_groups(pl, L);
+  const int ng = (int)pl.groups.size();
+  pl.group_of.assign(nl, 0);
+  pl.jb0.assign(nl, 0);
   int64_t base_items = 0;
-  for (int l = 0; l < nl; ++l) {
-    pl.ubs[l] = (int)((L[l].w2 + pl.cols2 - 1) / pl.cols2);
-    base_items += pl.B * pl.ubs[l];
+  for (int gi = 0; gi < ng; ++gi) {
+    PassGroup& g = pl.groups[gi];
+    for (size_t j = 0; j < g.members.size(); ++j) {
+      pl.group_of[g.members[j]] = gi;
+      pl.jb0[g.members[j]] = (int)j * pl.NCB;
+    }
+    g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
+    base_items += pl.B * g.ubs;
   }
   pl.nsplit = 1;
   if (base_items < kTargetItems) {
@@ -103,43 +159,53 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return L[a].w1 > L[b].w1; });
   pl.k1_begin.assign(nl, 0);
   pl.n1.assign(nl, 0);
+  pl.n_pack.assign(nl, 0);
   pl.total1 = 0;
   for (int l : order) {
     pl.k1_begin[l] = (int)pl.total1;
     pl.n1[l] = (int)(pl.B * pl.rbs);
     pl.total1 += pl.n1[l];
   }
-  pl.k2_begin.assign(nl, 0);
-  pl.n2.assign(nl, 0);
-  pl.slot_base.assign(nl, 0);
-  pl.n_pack.assign(nl, 0);
+  for (int l = 0; l < nl; ++l) pl.n_pack[l] = (int)(L[l].nsamples * packed_units(pl, L[l].w1));
+  // stage-2 items, one contiguous range per group width
+  pl.class_ncb.clear();
+  pl.class_begin.clear();
+  pl.class_end.clear();
   pl.total2 = 0;
   pl.slots = 0;
-  for (int l = 0; l < nl; ++l) {
-    pl.k2_begin[l] = (int)pl.total2;
-    pl.n2[l] = (int)(pl.B * pl.ubs[l] * pl.nsplit);
-    pl.total2 += pl.n2[l];
-    pl.slot_base[l] = pl.slots;
-    pl.slots += pl.ubs[l] * (pl.nsplit > 1 ? ysum_chunks(pl.cols2, pl.NCB) : 1);
-    pl.n_pack[l] = (int)(L[l].nsamples * packed_units(pl, L[l].w1));
+  for (int ncb : {1, 2, 3, 4, 6}) {
+    const int64_t begin = pl.total2;
+    for (PassGroup& g : pl.groups) {
+      if (g.ncb != ncb) continue;
+      g.k2_begin = (int)pl.total2;
+      g.n2 = (int)(pl.B * g.ubs * pl.nsplit);
+      pl.total2 += g.n2;
+      g.slot_base = pl.slots;
+      pl.slots += g.ubs * (pl.nsplit > 1 ? ysum_chunks(pl.cols2, g.ncb) : 1);
+    }
+    if (pl.total2 > begin) {
+      pl.class_ncb.push_back(ncb);
+      pl.class_begin.push_back((int)begin);
+      pl.class_end.push_back((int)pl.total2);
+    }
   }
-  pl.off_recs = bump.take(sizeof(LayerRec) * nl);
+  pl.off_recs = bump.take(sizeof(LayerRec) * (nl + ng));
   pl.off_items1 = bump.take(sizeof(int4) * pl.total1);
   pl.off_items2 = bump.take(sizeof(int4) * pl.total2);
   pl.off_partials = bump.take(sizeof(double2) * pl.B * pl.slots);
   pl.off_W.assign(nl, 0);
-  pl.off_V.assign(nl, 0);
-  pl.off_Yp.assign(nl, 0);
   const size_t unit = pl.bf16 ? 16 : 4;
-  for (int l = 0; l < nl; ++l) {
-    pl.off_W[l] = bump.take(unit * (size_t)pl.n_pack[l]);
-    pl.off_V[l] = bump.take((size_t)pl.B * pl.Tpad * NC * 4);
-    if (pl.nsplit > 1) pl.off_Yp[l] = bump.take((size_t)pl.nsplit * pl.B * L[l].w2 * NC * 4);
+  for (int l = 0; l < nl; ++l) pl.off_W[l] = bump.take(unit * (size_t)pl.n_pack[l]);
+  for (PassGroup& g : pl.groups) {
+    g.off_V = bump.take((size_t)pl.B * pl.Tpad * 16 * g.ncb * 4);
+    g.off_Yp = pl.nsplit > 1 ? bump.take((size_t)pl.nsplit * pl.B * L[g.members[0]].w2 * 16 * g.ncb * 4) : 0;
   }
 }
 
 int pass_launches(const PassPlan& pl, int nl) {
-  return (nl + kPrepChunk - 1) / kPrepChunk + 2 + (pl.needs_ysum() ? 1 : 0);
+  const int entries = nl + (int)pl.groups.size();
+  const int classes = (int)pl.class_ncb.size();
+  return (entries + kPrepChunk - 1) / kPrepChunk + 1 + classes * (pl.needs_ysum() ? 2 : 1);
 }
 
 // Optional event trace around each launch.
@@ -164,15 +230,17 @@ struct Tracer {
     if (e_ != hipSuccess) return e_;               \
   } while (0)
 
+// Prepare-table entries: entry e < nl is layer e (stage 1), entry nl + g is
+// stage-2 group g; the record of entry e is recs[e].
 hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, hipStream_t s,
                     Tracer& tr) {
   const int nl = (int)L.size();
-  const int NC = 16 * pl.NCB;
-  (void)NC;
+  const int ng = (int)pl.groups.size();
+  const int entries = nl + ng;
   LayerRec* recs = (LayerRec*)(base + pl.off_recs);
   int4* items1 = (int4*)(base + pl.off_items1);
   int4* items2 = (int4*)(base + pl.off_items2);
-  for (int c0 = 0; c0 < nl; c0 += kPrepChunk) {
+  for (int c0 = 0; c0 < entries; c0 += kPrepChunk) {
     PrepArgs a;
     std::memset(&a, 0, sizeof(a));
     a.recs = recs;
@@ -184,38 +252,53 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
     a.rbs = pl.rbs;
     a.nsplit = pl.nsplit;
     int units = 0;
-    const int cn = std::min(kPrepChunk, nl - c0);
+    const int cn = std::min(kPrepChunk, entries - c0);
     for (int j = 0; j < cn; ++j) {
-      const int l = c0 + j;
-      const PassLayer& in = L[l];
+      const int e = c0 + j;
       PrepLayer& P = a.L[j];
       LayerRec& R = P.rec;
-      R.X1 = in.X1;
-      R.X2 = in.X2;
-      R.W = base + pl.off_W[l];
-      R.V = base + pl.off_V[l];
-      R.Ypart = pl.nsplit > 1 ? (float*)(base + pl.off_Yp[l]) : (pl.store ? in.Yout : nullptr);
-      R.Yout = in.Yout;
-      R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
-      R.w1 = (int32_t)in.w1;
-      R.w2 = (int32_t)in.w2;
-      R.slot_base = pl.slot_base[l];
-      R.split = in.split;
-      P.wsrc = in.wsrc;
-      P.wsrc_stride_b = in.wsrc_stride_b;
-      P.wsrc_type = in.wsrc_type;
-      P.ld = (int32_t)in.ld;
-      P.ncols = in.ncols;
-      P.nsamples = in.nsamples;
-      P.layer = l;
+      R.split = 1 << 30;
+      if (e < nl) {  // stage-1 projection
+        const PassLayer& in = L[e];
+        const PassGroup& g = pl.groups[pl.group_of[e]];
+        R.X1 = in.X1;
+        R.W = base + pl.off_W[e];
+        R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
+        R.w1 = (int32_t)in.w1;
+        if (pl.bf16) {
+          R.V = (uint4*)(base + g.off_V) + (size_t)pl.jb0[e] * 2 * 64;
+          R.vstride = g.ncb * 2 * 64;
+        } else {
+          R.V = (float*)(base + g.off_V) + (size_t)pl.jb0[e] * 16;
+          R.vstride = 16 * g.ncb;
+        }
+        P.wsrc = in.wsrc;
+        P.wsrc_stride_b = in.wsrc_stride_b;
+        P.wsrc_type = in.wsrc_type;
+        P.ld = (int32_t)in.ld;
+        P.ncols = in.ncols;
+        P.nsamples = in.nsamples;
+        P.n_pack = pl.n_pack[e];
+        P.k1_begin = pl.k1_begin[e];
+        P.n1 = pl.n1[e];
+      } else {  // stage-2 group
+        const PassGroup& g = pl.groups[e - nl];
+        const PassLayer& in = L[g.members[0]];
+        R.X2 = in.X2;
+        R.V = base + g.off_V;
+        R.vstride = pl.bf16 ? g.ncb * 2 * 64 : 16 * g.ncb;
+        R.Ypart = pl.nsplit > 1 ? (float*)(base + g.off_Yp) : (pl.store ? in.Yout : nullptr);
+        R.Yout = in.Yout;
+        R.w2 = (int32_t)in.w2;
+        R.slot_base = g.slot_base;
+        R.split = in.split;
+        P.k2_begin = g.k2_begin;
+        P.n2 = g.n2;
+        P.ubs = g.ubs;
+      }
+      P.layer = e;
       P.unit_begin = units;
-      P.n_pack = pl.n_pack[l];
-      P.k1_begin = pl.k1_begin[l];
-      P.n1 = pl.n1[l];
-      P.k2_begin = pl.k2_begin[l];
-      P.n2 = pl.n2[l];
-      P.ubs = pl.ubs[l];
-      units += (P.n_pack + P.n1 + P.n2 + 1 + 255) / 256 * 256;  // next layer starts a work group
+      units += (P.n_pack + P.n1 + P.n2 + 1 + 255) / 256 * 256;  // next entry starts a work group
     }
     a.nlayers = cn;
     a.total_units = units;
@@ -236,14 +319,15 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, s));
   DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
 
-  st.items = items2;
-  st.n_items = (int32_t)pl.total2;
-  DPN_TRY(launch_tcontract(st, pl.bf16, pl.NCB, pl.direct(), s));
-  DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
-
-  if (pl.needs_ysum()) {
-    DPN_TRY(launch_ysum(st, pl.NCB, pl.cols2, pl.store ? MODE_STORE : MODE_SQ, s));
-    DPN_TRY(tr.mark(DPNORM_KERNEL_YSUM));
+  for (size_t c = 0; c < pl.class_ncb.size(); ++c) {
+    st.items = items2 + pl.class_begin[c];
+    st.n_items = pl.class_end[c] - pl.class_begin[c];
+    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.direct(), s));
+    DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
+    if (pl.needs_ysum()) {
+      DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, s));
+      DPN_TRY(tr.mark(DPNORM_KERNEL_YSUM));
+    }
   }
   return hipSuccess;
 }
@@ -294,8 +378,9 @@ struct HutchCall {
   size_t bytes = 0;
 };
 
+// fuse: layers that share A (same pointer and d) share one stage-2 pass.
 dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
-                          bool need_ptrs, HutchCall& hc) {
+                          bool need_ptrs, bool fuse, HutchCall& hc) {
   if (!layers) return DPNORM_ERR_NULL;
   if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
   if (L < 1 || L > (1 << 20)) return DPNORM_ERR_SIZE;
@@ -330,6 +415,7 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
   p.B = B;
   p.T = T;
   p.store = false;
+  p.fuse = fuse;
   Bump bump;
   plan_pass(p, hc.layers, bump);
   hc.bytes = align_up(bump.off);
@@ -340,8 +426,15 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
                          float* n, int accumulate, float* c, float C, void* ws, size_t ws_bytes, hipStream_t stream,
                          dpnorm_trace* trace) {
   HutchCall hc;
-  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, hc);
+  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, hc);
   if (st != DPNORM_OK) return st;
+  // A workspace sized without knowing which layers share A (a query with
+  // NULL pointers) may be too small for the fused plan: run unfused then.
+  if (ws_bytes < hc.bytes) {
+    HutchCall plain;
+    if (build_hutch(layers, L, dt, B, T, k, true, false, plain) == DPNORM_OK && ws_bytes >= plain.bytes)
+      hc = std::move(plain);
+  }
   if (!n) return DPNORM_ERR_NULL;
   if (accumulate != 0 && accumulate != 1) return DPNORM_ERR_VALUE;
   if (!aligned(n, 4) || (c && !aligned(c, 4))) return DPNORM_ERR_ALIGN;
@@ -491,6 +584,13 @@ const char* dpnorm_status_string(int status) {
   }
 }
 
+dpnorm_status dpnorm_read_probe(const void* buf, int64_t bytes, hipStream_t stream) {
+  if (!buf) return DPNORM_ERR_NULL;
+  if (bytes <= 0 || bytes % 16384 != 0 || bytes > ((int64_t)1 << 44)) return DPNORM_ERR_SIZE;
+  if (!aligned(buf, 16)) return DPNORM_ERR_ALIGN;
+  return hip_status(launch_read_probe(buf, bytes, stream));
+}
+
 dpnorm_status dpnorm_hutchpp_split(int64_t k, int64_t* m_s, int64_t* m_t) {
   if (!m_s || !m_t) return DPNORM_ERR_NULL;
   if (k < 3 || k > 96) return DPNORM_ERR_SIZE;
@@ -508,7 +608,7 @@ dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int6
   y.d = d;
   y.p = p;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, hc);
+  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, true, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;
@@ -518,7 +618,7 @@ dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t
                                              int64_t T, int64_t k, size_t* bytes) {
   if (!bytes) return DPNORM_ERR_NULL;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, hc);
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;

@@ -36,6 +36,9 @@ struct LayerRec {
   int32_t slot_base;   // first partial slot of this layer within a sample (per column block, or
                        // per column block and tile chunk when T is split)
   int32_t split;       // columns < split go to the first sum, the rest to the second
+  int32_t vstride;     // V units between consecutive 32-row chunks (bf16: uint4 fragments) or rows (fp32:
+                       // floats); several projections that share X2 write side by side into one V
+  int32_t pad_;
 };
 
 // Host-filled description used by the prepare kernel.
@@ -54,6 +57,9 @@ struct PrepLayer {
   int32_t ubs;             // stage-2 column blocks of X2 per sample
   int32_t pad_;
 };
+// An entry of the prepare table describes a stage-1 projection (packed W and
+// stage-1 items), a stage-2 group (stage-2 items), or both; n_pack, n1 or n2
+// is zero for the parts an entry does not have.
 
 struct PrepArgs {
   PrepLayer L[kPrepChunk];
@@ -83,6 +89,7 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
 hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStream_t s);
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
+// NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).
 hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s);
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s);
 // work groups of the split-T reduction per (layer, sample, column block)
@@ -104,5 +111,8 @@ hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const voi
 void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots);
 hipError_t launch_exact(const void* A, const void* G, bool bf16, bool gram, int32_t B, int32_t T, int32_t d,
                         int32_t p, double2* partials, hipStream_t s);
+
+// Read-only stream of `bytes` (a positive multiple of 16384) from buf.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, hipStream_t s);
 
 }  // namespace dpn

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
   }
 
   if (r0 + 32 * wv >= T) return;  // chunk past the sequence: stage 2 never reads it
-  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32 + wv) * (NCB * 2 * 64) + lane;
+  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32 + wv) * L->vstride + lane;
 #pragma unroll
   for (int jb = 0; jb < NCB; ++jb) {
     uint32_t hi[8], lo[8];
@@ -295,13 +295,14 @@ __global__ void __launch_bounds__(256) k_rowproj_f32(StageArgs a) {
       }
   }
 
-  float* out = (float*)L->V + ((int64_t)i * a.Tpad + r0) * NC;
+  const int vs = L->vstride;
+  float* out = (float*)L->V + ((int64_t)i * a.Tpad + r0) * vs;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(16 * mt + 4 * g + r) * NC + 16 * jb + n] = acc[mt][jb][r];
+      for (int r = 0; r < 4; ++r) out[(16 * mt + 4 * g + r) * vs + 16 * jb + n] = acc[mt][jb][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -658,10 +659,14 @@ hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct,
   if (bf16) {
     if (NCB == 1) DPN_TC(k_tcontract_bf16, 1);
     else if (NCB == 2) DPN_TC(k_tcontract_bf16, 2);
-    else DPN_TC(k_tcontract_bf16, 4);
+    else if (NCB == 3) DPN_TC(k_tcontract_bf16, 3);
+    else if (NCB == 4) DPN_TC(k_tcontract_bf16, 4);
+    else DPN_TC(k_tcontract_bf16, 6);
   } else {
     if (NCB == 1) DPN_TC(k_tcontract_f32, 1);
     else if (NCB == 2) DPN_TC(k_tcontract_f32, 2);
+    else if (NCB == 3) DPN_TC(k_tcontract_f32, 3);
+    else if (NCB == 6) DPN_TC(k_tcontract_f32, 6);
     else DPN_TC(k_tcontract_f32, 4);
   }
 #undef DPN_TC

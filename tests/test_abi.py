@@ -92,6 +92,36 @@ def test_grouped_workspace_covers_layers(lib):
     assert lib.dpnorm_hutch_grouped_workspace(None, 1, _lib.BF16, 2, 100, 8, C.byref(nb)) == _lib.ERR_NULL
 
 
+def shared_input_layers(n_layers, dm=128, kv=64, hid=256):
+    """Fake descriptors of a transformer stack in which q, k, v share one
+    input and gate, up share another (distinct aligned fake addresses)."""
+    shapes = [(dm, dm), (dm, kv), (dm, kv), (dm, dm), (dm, hid), (dm, hid), (hid, dm)]
+    input_of = (0, 0, 0, 3, 4, 4, 6)
+    arr = (_lib.Layer * (7 * n_layers))()
+    for layer in range(n_layers):
+        for j, (d, p) in enumerate(shapes):
+            a = 0x10000000 + (7 * layer + input_of[j]) * 0x100000
+            g = 0x80000000 + (7 * layer + j) * 0x100000
+            arr[7 * layer + j] = _lib.Layer(a, g, g + 0x80000, d, p)
+    return arr
+
+
+def test_grouped_workspace_shared_inputs(lib):
+    # 16 layers, B = 10, T = 1024: unshared, 1120 stage-2 items need no T
+    # split; shared, 640 items split T in two and need the partial tiles
+    arr = shared_input_layers(16)
+    plain = (_lib.Layer * len(arr))(*[_lib.Layer(None, None, None, y.d, y.p) for y in arr])
+    shared_b, plain_b = C.c_size_t(0), C.c_size_t(0)
+    assert lib.dpnorm_hutch_grouped_workspace(arr, len(arr), _lib.BF16, 10, 1024, 32, C.byref(shared_b)) == _lib.OK
+    assert lib.dpnorm_hutch_grouped_workspace(plain, len(arr), _lib.BF16, 10, 1024, 32, C.byref(plain_b)) == _lib.OK
+    assert shared_b.value > plain_b.value > 0
+    # one byte below both plans: rejected before anything is enqueued
+    n = C.c_void_p(N_ADDR)
+    st = lib.dpnorm_hutch_grouped(arr, len(arr), _lib.BF16, 10, 1024, 32, n, 0, None, 1.0, WS_ADDR,
+                                  plain_b.value - 1, None)
+    assert st == _lib.ERR_WORKSPACE
+
+
 def hutch(lib, A=A_ADDR, G=G_ADDR, P=P_ADDR, dt=_lib.BF16, B=2, T=100, d=64, p=32, k=8, n=N_ADDR, acc=0,
           ws=WS_ADDR, ws_bytes=None):
     if ws_bytes is None:
@@ -150,6 +180,13 @@ def test_clip_factor_checks(lib):
     assert lib.dpnorm_clip_factors(N_ADDR, 4, float("nan"), N_ADDR, None) == _lib.ERR_VALUE
     assert lib.dpnorm_clip_factors(N_ADDR, 4, 1.0, N_ADDR + 4, None) == _lib.ERR_VALUE
     assert lib.dpnorm_clip_factors(N_ADDR + 2, 4, 1.0, N_ADDR + 64, None) == _lib.ERR_ALIGN
+
+
+def test_read_probe_checks(lib):
+    assert lib.dpnorm_read_probe(None, 16384, None) == _lib.ERR_NULL
+    for bad in (0, -16384, 16383, 16384 + 8):
+        assert lib.dpnorm_read_probe(A_ADDR, bad, None) == _lib.ERR_SIZE
+    assert lib.dpnorm_read_probe(A_ADDR + 8, 16384, None) == _lib.ERR_ALIGN
 
 
 def test_event_helpers_reject_null(lib):

@@ -143,6 +143,37 @@ def config3_shapes() -> List[Tuple[int, int]]:
     return [(d, p) for _ in range(LLAMA_1B_LAYERS) for (_, d, p) in LLAMA_1B_PROJECTIONS]
 
 
+# Which projection's input each projection of a decoder layer reads in the
+# real model: q, k and v read the attention input; gate and up read the MLP
+# input; o and down read their own.
+LLAMA_1B_INPUT_OF: Tuple[int, ...] = (0, 0, 0, 3, 4, 4, 6)
+
+
+def shared_input_stack(device="cpu", B: int = 4, T: int = 4096, k: int = 32, layers: int = LLAMA_1B_LAYERS,
+                       dtype=torch.bfloat16) -> List[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]]:
+    """The Llama-3.2-1B-shaped stack with the inputs shared as in the real
+    model (workload 6 of the seed rule): per decoder layer four activation
+    tensors (attention input for q, k, v; o input; MLP input for gate, up;
+    down input), each s_A N(0,1) with s_A ~ U[0.5, 2]; per projection its own
+    G ~ s_G N(0,1) (s_G ~ U[0.5, 2]) and P ~ N(0, 1/k). Returns (A, G, P)
+    triples in the order q, k, v, o, gate, up, down per layer; projections
+    that share an input hold the same A tensor object."""
+    out = []
+    for layer in range(layers):
+        inputs = {}
+        for j, (_, d, p) in enumerate(LLAMA_1B_PROJECTIONS):
+            index = 7 * layer + j
+            src = 7 * layer + LLAMA_1B_INPUT_OF[j]
+            if src not in inputs:
+                s_a = 0.5 + 1.5 * float(torch.rand(1, generator=_gen("cpu", seed_of(6, src, ROLE_SCALE)))[0])
+                inputs[src] = gaussian((B, T, d), s_a, seed_of(6, src, ROLE_A), device, dtype)
+            s_g = 0.5 + 1.5 * float(torch.rand(2, generator=_gen("cpu", seed_of(6, index, ROLE_SCALE)))[1])
+            G = gaussian((B, T, p), s_g, seed_of(6, index, ROLE_G), device, dtype)
+            P = projection(p, k, seed_of(6, index, ROLE_P), device, dtype)
+            out.append((inputs[src], G, P))
+    return out
+
+
 def hutchpp_split(k: int) -> Tuple[int, int]:
     """Budget split used by the Hutch++ workloads: ceil(k/3) sketch columns,
     the same number of head columns, and k - 2 ceil(k/3) tail columns."""
