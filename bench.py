@@ -156,6 +156,62 @@ def shared_input_stack(args):
     return out
 
 
+def dpsgd_rc_step(args):
+    """One DP-SGD-RC training step (forward, backward 1, norm path, clip,
+    backward 2, noise, Adam) on a randomly initialised Llama-shaped stack at
+    Llama-3.2-1B widths (2 decoder layers, B=4, T=2048, bf16; attention in
+    float32), with a non-private step (forward, one backward, Adam) on the
+    same model beside it."""
+    import torch
+    import sample_grad_norms_amd as dp
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    from workloads import llama_block as lb
+    dev = torch.device("cuda:0")
+    shape = dict(layers=2, dim=2048, heads=32, kv_heads=8, hidden=8192, vocab=2048)
+    B, T = 4, 2048
+    model = lb.build(90, device=dev, dtype=torch.bfloat16, **shape)
+    x, y = lb.batch(91, B, T, shape["dim"], shape["vocab"], device=dev, dtype=torch.bfloat16)
+    timer = dp.KernelTimer(64)
+    rc = RandomizedClipping(model, C=1.0, noise_multiplier=1.0, k=32, timer=timer)
+    opt = torch.optim.Adam(rc.params, lr=1e-5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    parts = {"forward": 0.0, "backward1_and_norms": 0.0, "backward2": 0.0, "noise_and_adam": 0.0}
+    norm_ms, reps = 0.0, 3
+    for r in range(reps + 1):
+        ev[0].record()
+        with rc.capture():
+            losses = lb.per_sample_loss(model(x), y)
+        ev[1].record()
+        n, c = rc.clip_factors(losses)
+        ev[2].record()
+        rc.clipped_backward(losses, c)
+        ev[3].record()
+        rc.add_noise()
+        opt.step()
+        opt.zero_grad(set_to_none=True)
+        ev[4].record()
+        torch.cuda.synchronize()
+        if r == 0:
+            continue
+        for j, key in enumerate(parts):
+            parts[key] += ev[j].elapsed_time(ev[j + 1]) / reps
+        norm_ms += sum(ms for _, ms in timer.last()) / reps
+    del losses, n, c
+
+    def plain():
+        loss = lb.per_sample_loss(model(x), y).mean()
+        loss.backward()
+        opt.step()
+        opt.zero_grad(set_to_none=True)
+    plain_ms = timed(plain, reps, 1)
+    step_ms = sum(parts.values())
+    rc.remove()
+    return {"model": "random-init Llama-3.2-1B-width stack, 2 decoder layers + output projection (vocab 2048)",
+            "B": B, "T": T, "dtype": "bf16", "k": 32, "step_ms": step_ms, "parts_ms": parts,
+            "norm_path_kernels_ms": norm_ms, "norm_path_share": norm_ms / step_ms,
+            "nonprivate_step_ms": plain_ms, "dpsgd_rc_over_nonprivate": step_ms / plain_ms}
+
+
 def extras(args):
     """Other workloads: single-layer Hutchinson, Hutch++ and the exact
     comparator, each timed the same way."""
@@ -326,7 +382,8 @@ def main():
     }
     if not args.no_extras:
         rec["extras"] = {"hbm_calibration": hbm_calibration(dev),
-                         "llama_shared_inputs_B4_T4096_k32": shared_input_stack(args)}
+                         "llama_shared_inputs_B4_T4096_k32": shared_input_stack(args),
+                         "dpsgd_rc_step_llama1b_width_2layers_B4_T2048": dpsgd_rc_step(args)}
         rec["extras"].update(extras(args))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(layers, B, T, max(1, min(16, args.cpu_layers)))

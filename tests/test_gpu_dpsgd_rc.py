@@ -1,0 +1,184 @@
+"""The DP-SGD-RC step around the norm path, on a randomly initialised
+Llama-shaped stack.
+
+Ground truth is per-sample gradients taken one sample at a time by autograd,
+in float64 on the CPU, on a copy of the same model. The exact estimator and a
+Hutchinson projection equal to the identity must reproduce their squared
+norms (a check of what the hooks record); the second backward pass must give
+sum_i c_i grad l_i; the noise must have standard deviation sigma C / B; and
+in bfloat16 the Hutchinson estimates must match the fp64 oracle run on the
+same recorded A, G and P.
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+from torch import nn
+
+import oracle
+from workloads import llama_block as lb
+
+pytestmark = pytest.mark.gpu
+
+TINY = dict(layers=1, dim=32, heads=2, kv_heads=1, hidden=64, vocab=16)   # every width <= 64
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def brute_force(model, x, y):
+    """Per-sample gradients of the linear weights, float64 on the CPU."""
+    ref = copy.deepcopy(model).double().cpu()
+    weights = [m.weight for m in ref.modules() if isinstance(m, nn.Linear)]
+    grads = []
+    for i in range(x.shape[0]):
+        loss = lb.per_sample_loss(ref(x[i:i + 1].double().cpu()), y[i:i + 1].cpu())[0]
+        grads.append([g.detach() for g in torch.autograd.grad(loss, weights)])
+    norms = np.array([sum(float((g ** 2).sum()) for g in gs) for gs in grads])
+    return grads, norms
+
+
+def rel(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return np.abs(a - b) / np.abs(b)
+
+
+def identity_projection(p, k, dtype, device, generator):
+    P = torch.zeros(p, k, dtype=dtype, device=device)
+    P[:, :p] = torch.eye(p, dtype=dtype, device=device)
+    return P
+
+
+@pytest.mark.parametrize("estimator", ["exact", "hutch_identity"])
+def test_norms_match_per_sample_gradients(estimator):
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    model = lb.build(71, device=dev(), **TINY)
+    x, y = lb.batch(72, 3, 12, TINY["dim"], TINY["vocab"], device=dev())
+    if estimator == "exact":
+        rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.0, estimator="exact")
+    else:  # k = 64 columns, P = [I | 0]: the estimate is the exact norm
+        rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.0, k=64, projection=identity_projection)
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, c = rc.clip_factors(losses)
+    torch.cuda.synchronize()
+    _, want = brute_force(model, x, y)
+    err = rel(n.cpu(), want)
+    print(f"{estimator}: max rel err vs per-sample gradients {err.max():.2e}", flush=True)
+    assert np.all(err <= 1e-4)   # float32 forward and backward on the GPU vs float64
+    np.testing.assert_allclose(c.cpu().numpy(), np.minimum(1.0 / np.sqrt(want), 1.0), rtol=1e-4)
+
+
+def test_clipped_gradient_and_noise():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    model = lb.build(73, device=dev(), **TINY)
+    B = 4
+    x, y = lb.batch(74, B, 10, TINY["dim"], TINY["vocab"], device=dev())
+    C = 0.5
+    rc = RandomizedClipping(model, C=C, noise_multiplier=0.0, estimator="exact")
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, c = rc.clip_factors(losses)
+    rc.clipped_backward(losses, c)
+    got = [p.grad.detach().double().cpu().clone() for p in rc.params]
+    grads, norms = brute_force(model, x, y)
+    cs = np.minimum(C / np.sqrt(norms), 1.0)
+    assert np.any(cs < 1.0)
+    for j, g in enumerate(got):
+        want = sum(cs[i] * grads[i][j] for i in range(B))
+        assert torch.allclose(g, want, rtol=1e-4, atol=1e-6 * float(want.abs().max())), f"weight {j}"
+    # every clipped per-sample gradient is within C
+    for i in range(B):
+        assert cs[i] * np.sqrt(norms[i]) <= C * (1 + 1e-9)
+    # sigma = 0: add_noise only divides by B
+    rc.add_noise()
+    for g0, p in zip(got, rc.params):
+        assert torch.allclose(p.grad.double().cpu(), g0 / B, rtol=1e-6)
+
+
+def test_noise_scale():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    model = lb.build(75, device=dev(), layers=1, dim=64, heads=2, kv_heads=1, hidden=128, vocab=32)
+    B, sigma, C = 4, 1.5, 0.8
+    x, y = lb.batch(76, B, 8, 64, 32, device=dev())
+    rc = RandomizedClipping(model, C=C, noise_multiplier=sigma, estimator="exact", seed=5)
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, c = rc.clip_factors(losses)
+    rc.clipped_backward(losses, c)
+    clean = [p.grad.detach().clone() for p in rc.params]
+    rc.add_noise()
+    z = torch.cat([((p.grad - g0 / B) * B / (sigma * C)).flatten() for p, g0 in zip(rc.params, clean)])
+    m, s = float(z.mean()), float(z.std())
+    print(f"noise: {z.numel()} entries, mean {m:.4f}, std {s:.4f}", flush=True)
+    assert abs(s - 1.0) < 0.03 and abs(m) < 0.03
+
+
+def test_weight_shared_module_is_concatenated_along_T():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+
+    class Twice(nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.lin = nn.Linear(16, 16, bias=False)
+            self.out = nn.Linear(16, 8, bias=False)
+
+        def forward(self, x):
+            return self.out(torch.tanh(self.lin(torch.tanh(self.lin(x)))))
+
+    torch.manual_seed(0)
+    model = Twice().to(dev())
+    x = torch.randn(3, 5, 16, device=dev())
+    y = torch.randint(0, 8, (3, 5), device=dev())
+    rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.0, estimator="exact")
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, _ = rc.clip_factors(losses)
+    ref = copy.deepcopy(model).double().cpu()
+    want = []
+    for i in range(3):
+        loss = lb.per_sample_loss(ref(x[i:i + 1].double().cpu()), y[i:i + 1].cpu())[0]
+        want.append(sum(float((g ** 2).sum()) for g in torch.autograd.grad(loss, list(ref.parameters()))))
+    err = rel(n.cpu(), want)
+    print(f"shared weight: max rel err {err.max():.2e}", flush=True)
+    assert np.all(err <= 1e-4)
+
+
+def test_bf16_llama_step_hutch_parity_and_update():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    shape = dict(layers=2, dim=256, heads=4, kv_heads=2, hidden=512, vocab=128)
+    model = lb.build(77, device=dev(), dtype=torch.bfloat16, **shape)
+    x, y = lb.batch(78, 4, 64, shape["dim"], shape["vocab"], device=dev(), dtype=torch.bfloat16)
+    rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.5, k=32, keep_layers=True)
+    opt = torch.optim.Adam(rc.params, lr=1e-3)
+    before = [p.detach().clone() for p in rc.params]
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, c = rc.step(losses, opt)
+    torch.cuda.synchronize()
+    # q, k, v (and gate, up) read one recorded input each: one copy is shared
+    ptrs = [A.data_ptr() for (A, _, _) in rc.last_layers]
+    assert len(set(ptrs)) == 4 * shape["layers"] + 1
+    want = oracle.layer_sum([oracle.hutch(A, G, P) for (A, G, P) in rc.last_layers])
+    err = rel(n.cpu(), want)
+    print(f"bf16 llama step: max rel err vs oracle {err.max():.2e}", flush=True)
+    assert np.all(err <= 1e-3)
+    np.testing.assert_allclose(c.cpu().numpy(), np.minimum(1.0 / np.sqrt(want), 1.0), rtol=1e-3)
+    for p, p0 in zip(rc.params, before):
+        assert torch.isfinite(p).all() and not torch.equal(p, p0)
+
+
+def test_other_estimators_run_in_the_step():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    shape = dict(layers=1, dim=64, heads=2, kv_heads=1, hidden=128, vocab=32)
+    model = lb.build(79, device=dev(), dtype=torch.bfloat16, **shape)
+    x, y = lb.batch(80, 3, 40, 64, 32, device=dev(), dtype=torch.bfloat16)
+    rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.0, estimator="hutchpp", k=24, keep_layers=True)
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, _ = rc.clip_factors(losses)
+    torch.cuda.synchronize()
+    assert torch.isfinite(n).all() and bool((n > 0).all())
+    assert all(P is not None and P.shape[1] == 8 for (_, _, P) in rc.last_layers)
