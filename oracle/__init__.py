@@ -10,6 +10,7 @@ from .reference import (  # noqa: F401
     exact_gram,
     exact_trace,
     hutch,
+    hutch_sign,
     hutch_trace_form,
     hutchpp,
     hutchpp_head_tail,
@@ -19,4 +20,5 @@ from .reference import (  # noqa: F401
     layer_sum,
     orthonormal_basis,
     to_f64,
+    unpack_signs,
 )

@@ -122,6 +122,35 @@ def hutch_trace_form(A, G, P) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Hutchinson with a +-1 projection [RC-note 实验关键数据 › 关键发现 and
+#  局限与展望: {-1,+1} 1-bit projection matrices in the style of Achlioptas
+#  shrink P; RC-nl Betekenis en Claims: +-1-valued sketches]
+# Reading: P = S / sqrt(k) with S in {-1,+1}^{p x k}, so that E[P P^T] = I as
+# for the N(0, 1/k) matrix and the estimate stays unbiased.
+# --------------------------------------------------------------------------
+
+def unpack_signs(S_bits, p: int, k: int) -> np.ndarray:
+    """S [p][k] in {-1,+1} from bit-packed rows of 32-bit words: entry (v, j)
+    is bit j % 32 of word j // 32 of row v, 0 meaning +1 and 1 meaning -1."""
+    if hasattr(S_bits, "detach"):
+        S_bits = S_bits.detach().to("cpu").numpy()
+    words = np.asarray(S_bits).view(np.uint32).reshape(p, -1)
+    S = np.empty((p, k))
+    for v in range(p):
+        for j in range(k):
+            bit = (int(words[v, j // 32]) >> (j % 32)) & 1
+            S[v, j] = -1.0 if bit else 1.0
+    return S
+
+
+def hutch_sign(A, G, S_bits, k: int) -> np.ndarray:
+    """n_hat_i = ||A_i^T (G_i P)||_F^2 with P = S / sqrt(k) and S the unpacked
+    signs (the same estimate as hutch with that P)."""
+    p = G.shape[-1]
+    return hutch(A, G, unpack_signs(S_bits, p, k) / math.sqrt(k))
+
+
+# --------------------------------------------------------------------------
 # Hutch++ [RC-note 关键设计 › Hutch++ 头-尾分解的低误差变体;
 #          RC-nl Kernmechanisme item 2]
 # --------------------------------------------------------------------------
