@@ -212,6 +212,26 @@ def dpsgd_rc_step(args):
             "nonprivate_step_ms": plain_ms, "dpsgd_rc_over_nonprivate": step_ms / plain_ms}
 
 
+def sign_projection_stack(args, layers):
+    """The Llama-3.2-1B-shaped stack with +-1 projections stored as bits
+    (dpnorm_hutch_sign_grouped) in place of the bf16 Gaussian P."""
+    import torch
+    import sample_grad_norms_amd as dp
+    dev = torch.device("cuda:0")
+    B, T, k = 4, 4096, 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    triples = [(A, G, dp.random_signs(G.shape[2], k, device=dev, generator=g)) for (A, G, _) in layers]
+    ws = torch.empty(dp.hutch_grouped_workspace(layers, torch.bfloat16, B, T, k), dtype=torch.uint8, device=dev)
+    n = torch.empty(B, dtype=torch.float32, device=dev)
+    c = torch.empty(B, dtype=torch.float32, device=dev)
+    ms = timed(lambda: dp.hutch_sign_grouped(triples, k, out=n, C_clip=1.0, clip_out=c, workspace=ws),
+               args.steps, args.warmup)
+    return {"ms_per_step": ms, "samples_tokens_per_s": B * T / (ms * 1e-3),
+            "projection_bytes_sign": sum(S.numel() * 4 for (_, _, S) in triples),
+            "projection_bytes_bf16": sum(P.numel() * 2 for (_, _, P) in layers)}
+
+
 def extras(args):
     """Other workloads: single-layer Hutchinson, Hutch++ and the exact
     comparator, each timed the same way."""
@@ -383,6 +403,7 @@ def main():
     if not args.no_extras:
         rec["extras"] = {"hbm_calibration": hbm_calibration(dev),
                          "llama_shared_inputs_B4_T4096_k32": shared_input_stack(args),
+                         "llama_stack_sign_projections_B4_T4096_k32": sign_projection_stack(args, layers),
                          "dpsgd_rc_step_llama1b_width_2layers_B4_T2048": dpsgd_rc_step(args)}
         rec["extras"].update(extras(args))
     if not args.no_cpu_baseline:

@@ -168,6 +168,30 @@ dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L,
                                           float* c, float C, void* ws, size_t ws_bytes,
                                           hipStream_t stream, dpnorm_trace* trace);
 
+/* Hutchinson estimate with a +-1 projection stored as bits (note: 实验关键数据
+ * › 关键发现 and 局限与展望, which name {-1,+1} 1-bit projections in the
+ * style of Achlioptas as the way to shrink P, the memory ceiling at large k;
+ * summary: Betekenis en Claims, +-1-valued sketches). The projection is
+ * P = S / sqrt(k) with S in {-1,+1}^{p x k} (E[P P^T] = I, as for the
+ * N(0, 1/k) matrix), so n_hat_i = ||A_i^T (G_i S)||_F^2 / k.
+ * S_bits is a device array [p][ceil(k/32)] of 32-bit words, 4-byte aligned:
+ * bit (j % 32) of word (j / 32) of row v is S[v][j], 0 for +1 and 1 for -1
+ * (bits past k are ignored); uniformly random words give i.i.d. Rademacher
+ * signs. p * ceil(k/32) * 4 bytes instead of p * k * 2 (bf16).
+ * The workspace is that of dpnorm_hutch / dpnorm_hutch_grouped with the same
+ * sizes. Other arguments, semantics and errors as dpnorm_hutch. The privacy
+ * accounting of such projections is outside this library. */
+dpnorm_status dpnorm_hutch_sign(const void* A, const void* G, const uint32_t* S_bits, dpnorm_dtype dt,
+                                int64_t B, int64_t T, int64_t d, int64_t p, int64_t k, float* n,
+                                int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* dpnorm_hutch_grouped with +-1 projections: layers[l].P points to layer l's
+ * S_bits as above. Layers sharing A share one pass over it, as there. */
+dpnorm_status dpnorm_hutch_sign_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
+                                        int64_t B, int64_t T, int64_t k, float* n, int accumulate,
+                                        float* c, float C, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
 /* Hutch++ estimate of one layer with budget k (note: 关键设计 › Hutch++;
  * summary: Kernmechanisme item 2). With (m_s, m_t) from
  * dpnorm_hutchpp_split(k), S is [p][m_s] (sketch, any scale; N(0,1)

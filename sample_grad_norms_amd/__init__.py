@@ -200,6 +200,85 @@ def hutch_grouped(layers: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     return (n, c) if c is not None else n
 
 
+def random_signs(p: int, k: int, device="cuda", generator: Optional[torch.Generator] = None) -> torch.Tensor:
+    """Uniformly random 32-bit words [p][ceil(k/32)] (int32 storage): the
+    bit-packed i.i.d. Rademacher signs of a +-1 projection (see hutch_sign)."""
+    return torch.randint(-2 ** 31, 2 ** 31, (p, (k + 31) // 32), dtype=torch.int32, device=device,
+                         generator=generator)
+
+
+def _sign_layer_array(layers, k: int):
+    if len(layers) == 0:
+        raise ValueError("at least one layer is needed")
+    A0 = layers[0][0]
+    _need(A0, "A", 3)
+    dtype, device = A0.dtype, A0.device
+    B, T = A0.shape[0], A0.shape[1]
+    if not 1 <= k <= 64:
+        raise ValueError("k must be in 1..64")
+    arr = (_lib.Layer * len(layers))()
+    for j, (A, G, S) in enumerate(layers):
+        _need(A, f"layers[{j}].A", 3, dtype)
+        _need(G, f"layers[{j}].G", 3, dtype)
+        _need(S, f"layers[{j}].S_bits", 2, torch.int32)
+        if A.device != device or G.device != device or S.device != device:
+            raise ValueError("all tensors of a call must be on one device")
+        if A.shape[:2] != (B, T) or G.shape[:2] != (B, T):
+            raise ValueError(f"layers[{j}]: A and G must be [B={B}][T={T}][*]")
+        if tuple(S.shape) != (G.shape[2], (k + 31) // 32):
+            raise ValueError(f"layers[{j}]: S_bits must be [p={G.shape[2]}][{(k + 31) // 32}] int32 words")
+        arr[j] = _lib.Layer(A.data_ptr(), G.data_ptr(), S.data_ptr(), A.shape[2], G.shape[2])
+    return arr, dtype, device, B, T
+
+
+def hutch_sign(A: torch.Tensor, G: torch.Tensor, S_bits: torch.Tensor, k: int, out: Optional[torch.Tensor] = None,
+               accumulate: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """n_hat_i = ||A_i^T (G_i S)||_F^2 / k with S in {-1,+1}^{p x k} stored as
+    bits (dpnorm_hutch_sign): S_bits is int32 [p][ceil(k/32)], bit j % 32 of
+    word j // 32 of row v set for S[v][j] = -1."""
+    _sign_layer_array([(A, G, S_bits)], k)
+    B, T = A.shape[0], A.shape[1]
+    L = lib()
+    nbytes = C.c_size_t(0)
+    _check(L.dpnorm_hutch_workspace(_code(A.dtype), B, T, A.shape[2], G.shape[2], k, C.byref(nbytes)),
+           "dpnorm_hutch_workspace")
+    n = _out(out, B, A.device, accumulate)
+    ws, wsp = _given_workspace(workspace, nbytes.value, A.device)
+    _check(L.dpnorm_hutch_sign(A.data_ptr(), G.data_ptr(), S_bits.data_ptr(), _code(A.dtype), B, T, A.shape[2],
+                               G.shape[2], k, n.data_ptr(), int(accumulate), wsp, nbytes.value, _stream(A.device)),
+           "dpnorm_hutch_sign")
+    return n
+
+
+def hutch_sign_grouped(layers, k: int, out: Optional[torch.Tensor] = None, accumulate: bool = False,
+                       C_clip: Optional[float] = None, clip_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """hutch_grouped with +-1 projections (dpnorm_hutch_sign_grouped): layers
+    are (A, G, S_bits) triples. Returns n, or (n, c) when C_clip is given."""
+    arr, dtype, device, B, T = _sign_layer_array(layers, k)
+    L = lib()
+    nbytes = C.c_size_t(0)
+    _check(L.dpnorm_hutch_grouped_workspace(arr, len(layers), _code(dtype), B, T, k, C.byref(nbytes)),
+           "dpnorm_hutch_grouped_workspace")
+    n = _out(out, B, device, accumulate)
+    c = None
+    if C_clip is not None:
+        c = _out(clip_out, B, device, False, "clip_out") if clip_out is not None else torch.empty_like(n)
+    if workspace is None:
+        ws, wsp = _workspace(nbytes.value, device)
+        ws_bytes = nbytes.value
+    else:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a GPU tensor")
+        ws, wsp = workspace, workspace.data_ptr()
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L.dpnorm_hutch_sign_grouped(arr, len(layers), _code(dtype), B, T, k, n.data_ptr(), int(accumulate),
+                                       c.data_ptr() if c is not None else None,
+                                       float(C_clip) if C_clip is not None else 1.0, wsp, ws_bytes,
+                                       _stream(device)), "dpnorm_hutch_sign_grouped")
+    return (n, c) if c is not None else n
+
+
 def read_probe(buf: torch.Tensor) -> None:
     """Calibration: stream the whole of ``buf`` (a contiguous GPU tensor whose
     size is a multiple of 16384 bytes) once with the stage kernels' direct

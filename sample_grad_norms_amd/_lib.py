@@ -43,6 +43,10 @@ SIGNATURES = {
     "dpnorm_status_string": ([C.c_int], C.c_char_p),
     "dpnorm_hutchpp_split": ([_i64, C.POINTER(_i64), C.POINTER(_i64)], C.c_int),
     "dpnorm_read_probe": ([_vp, _i64, _vp], C.c_int),
+    "dpnorm_hutch_sign": ([_vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _sz, _vp],
+                          C.c_int),
+    "dpnorm_hutch_sign_grouped": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32,
+                                   _vp, _sz, _vp], C.c_int),
     "dpnorm_hutch_workspace": ([C.c_int, _i64, _i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "dpnorm_hutch_grouped_workspace": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "dpnorm_hutch": ([_vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _sz, _vp], C.c_int),

@@ -379,8 +379,10 @@ struct HutchCall {
 };
 
 // fuse: layers that share A (same pointer and d) share one stage-2 pass.
+// sign: each layer's P is bit-packed +-1 ([p][ceil(k/32)] 32-bit words); the
+// 1/sqrt(k) scale of the entries is applied as 1/k on the finished sums.
 dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
-                          bool need_ptrs, bool fuse, HutchCall& hc) {
+                          bool need_ptrs, bool fuse, bool sign, HutchCall& hc) {
   if (!layers) return DPNORM_ERR_NULL;
   if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
   if (L < 1 || L > (1 << 20)) return DPNORM_ERR_SIZE;
@@ -393,7 +395,7 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
     if (st != DPNORM_OK) return st;
     if (need_ptrs) {
       if (!y.A || !y.G || !y.P) return DPNORM_ERR_NULL;
-      if (!aligned(y.A, 16) || !aligned(y.G, 16) || !aligned(y.P, esize(dt))) return DPNORM_ERR_ALIGN;
+      if (!aligned(y.A, 16) || !aligned(y.G, 16) || !aligned(y.P, sign ? 4 : esize(dt))) return DPNORM_ERR_ALIGN;
     }
     PassLayer& pl = hc.layers[l];
     pl.X1 = y.G;
@@ -401,8 +403,8 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
     pl.w1 = y.p;
     pl.w2 = y.d;
     pl.wsrc = y.P;
-    pl.wsrc_type = dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32;
-    pl.ld = k;
+    pl.wsrc_type = sign ? SRC_SIGN : (dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32);
+    pl.ld = sign ? (k + 31) / 32 : k;
     pl.ncols = (int)k;
     items1 += B * ((T + kRowsK1 - 1) / kRowsK1);
     items2 += B * ((y.d + kColsK2F32 - 1) / kColsK2F32) * 64;
@@ -424,15 +426,15 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
 
 dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
                          float* n, int accumulate, float* c, float C, void* ws, size_t ws_bytes, hipStream_t stream,
-                         dpnorm_trace* trace) {
+                         dpnorm_trace* trace, bool sign = false) {
   HutchCall hc;
-  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, hc);
+  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, sign, hc);
   if (st != DPNORM_OK) return st;
   // A workspace sized without knowing which layers share A (a query with
   // NULL pointers) may be too small for the fused plan: run unfused then.
   if (ws_bytes < hc.bytes) {
     HutchCall plain;
-    if (build_hutch(layers, L, dt, B, T, k, true, false, plain) == DPNORM_OK && ws_bytes >= plain.bytes)
+    if (build_hutch(layers, L, dt, B, T, k, true, false, sign, plain) == DPNORM_OK && ws_bytes >= plain.bytes)
       hc = std::move(plain);
   }
   if (!n) return DPNORM_ERR_NULL;
@@ -450,7 +452,8 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
   const size_t e = esize(dt);
   for (int64_t l = 0; l < L; ++l) {
     const dpnorm_layer& y = layers[l];
-    const size_t sa = (size_t)B * T * y.d * e, sg = (size_t)B * T * y.p * e, sp = (size_t)y.p * k * e;
+    const size_t sa = (size_t)B * T * y.d * e, sg = (size_t)B * T * y.p * e;
+    const size_t sp = sign ? (size_t)y.p * ((k + 31) / 32) * 4 : (size_t)y.p * k * e;
     for (const float* o : {(const float*)n, (const float*)c}) {
       if (!o) continue;
       if (overlaps(o, nb, y.A, sa) || overlaps(o, nb, y.G, sg) || overlaps(o, nb, y.P, sp)) return DPNORM_ERR_VALUE;
@@ -471,7 +474,7 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
   if (he == hipSuccess) he = run_pass(hc.plan, hc.layers, (char*)ws, stream, tr);
   if (he == hipSuccess)
     he = launch_finish((const double2*)((char*)ws + hc.plan.off_partials), (int32_t)B, hc.plan.slots, n, accumulate,
-                       nullptr, nullptr, c, c ? C : 1.f, c ? 1 : 0, stream);
+                       nullptr, nullptr, c, c ? C : 1.f, c ? 1 : 0, sign ? 1.0 / (double)k : 1.0, stream);
   if (he == hipSuccess) he = tr.mark(DPNORM_KERNEL_FINISH);
   return hip_status(he);
 }
@@ -608,7 +611,7 @@ dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int6
   y.d = d;
   y.p = p;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, true, hc);
+  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, true, false, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;
@@ -618,7 +621,7 @@ dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t
                                              int64_t T, int64_t k, size_t* bytes) {
   if (!bytes) return DPNORM_ERR_NULL;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, hc);
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, false, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;
@@ -647,6 +650,24 @@ dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L,
                                           void* ws, size_t ws_bytes, hipStream_t stream, dpnorm_trace* trace) {
   if (!trace) return DPNORM_ERR_NULL;
   return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, trace);
+}
+
+dpnorm_status dpnorm_hutch_sign(const void* A, const void* G, const uint32_t* S_bits, dpnorm_dtype dt, int64_t B,
+                                int64_t T, int64_t d, int64_t p, int64_t k, float* n, int accumulate, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  dpnorm_layer y;
+  y.A = A;
+  y.G = G;
+  y.P = S_bits;
+  y.d = d;
+  y.p = p;
+  return hutch_impl(&y, 1, dt, B, T, k, n, accumulate, nullptr, 1.f, ws, ws_bytes, stream, nullptr, true);
+}
+
+dpnorm_status dpnorm_hutch_sign_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T,
+                                        int64_t k, float* n, int accumulate, float* c, float C, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, nullptr, true);
 }
 
 dpnorm_status dpnorm_hutchpp_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, int64_t k,
@@ -701,7 +722,7 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr);
   if (he == hipSuccess)
     he = launch_finish((const double2*)(base + hc.p3.off_partials), (int32_t)B, hc.p3.slots, n, accumulate, head,
-                       tail, nullptr, 1.f, 0, stream);
+                       tail, nullptr, 1.f, 0, 1.0, stream);
   if (he == hipSuccess && rank) he = hipMemcpyAsync(rank, rk, nb, hipMemcpyDeviceToDevice, stream);
   return hip_status(he);
 }
@@ -733,7 +754,7 @@ dpnorm_status dpnorm_exact(const void* A, const void* G, dpnorm_dtype dt, int64_
   hipError_t he = launch_exact(A, G, dt == DPNORM_BF16, gram, (int32_t)B, (int32_t)T, (int32_t)d, (int32_t)p,
                                (double2*)ws, stream);
   if (he == hipSuccess)
-    he = launch_finish((const double2*)ws, (int32_t)B, slots, n, accumulate, nullptr, nullptr, nullptr, 1.f, 0,
+    he = launch_finish((const double2*)ws, (int32_t)B, slots, n, accumulate, nullptr, nullptr, nullptr, 1.f, 0, 1.0,
                        stream);
   return hip_status(he);
 }

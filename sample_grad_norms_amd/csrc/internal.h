@@ -21,7 +21,7 @@ constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 1024;  // elements of a Y tile per split-T reduction work group
 constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
 
-enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1 };
+enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1, SRC_SIGN = 2 };  // SIGN: bit-packed +-1, ld in 32-bit words
 
 // Device-side description of one layer (written by the prepare kernel).
 struct LayerRec {
@@ -94,8 +94,9 @@ hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct,
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s);
 // work groups of the split-T reduction per (layer, sample, column block)
 inline int ysum_chunks(int cols_per_block, int NCB) { return (cols_per_block * 16 * NCB + kYsumChunk - 1) / kYsumChunk; }
+// n (+)= scale * (sum of both partial sums); head / tail get the scaled sums.
 hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, float* n, int accumulate,
-                         float* head, float* tail, float* c, float C, int with_clip, hipStream_t s);
+                         float* head, float* tail, float* c, float C, int with_clip, double scale, hipStream_t s);
 hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s);
 
 // Hutch++: orthonormal basis Q of the sketch X [B][p][MP] (MP = 16 or 32

@@ -30,6 +30,18 @@ __device__ __forceinline__ float load_src(const void* p, int64_t idx, int type) 
   return ((const float*)p)[idx];
 }
 
+// Element (v, c) of sample smp's W source. Sign sources hold one bit per
+// entry, 32 columns to a word (bit c % 32 of word c / 32 of row v): 0 is +1,
+// 1 is -1; the 1/sqrt(k) scale is applied to the finished sums instead.
+__device__ __forceinline__ float w_value(const PrepLayer& P, int smp, int v, int c) {
+  const int64_t row = smp * P.wsrc_stride_b + (int64_t)v * P.ld;
+  if (P.wsrc_type == SRC_SIGN) {
+    const uint32_t word = ((const uint32_t*)P.wsrc)[row + (c >> 5)];
+    return ((word >> (c & 31)) & 1u) ? -1.f : 1.f;
+  }
+  return load_src(P.wsrc, row + c, P.wsrc_type);
+}
+
 __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
   const int first = blockIdx.x * 256;
   int l = 0;
@@ -63,8 +75,7 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
       for (int s = 0; s < 8; ++s) {
         const int v = v0 + s;
         float x = 0.f;
-        if (v < rows && c < P.ncols)
-          x = load_src(P.wsrc, smp * P.wsrc_stride_b + (int64_t)v * P.ld + c, P.wsrc_type);
+        if (v < rows && c < P.ncols) x = w_value(P, smp, v, c);
         uint32_t hi, lo;
         split_bf16(x, hi, lo);
         b[s] = h ? lo : hi;
@@ -79,8 +90,7 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
       const int q = r - smp * per_s;
       const int v = q / NC, c = q - v * NC;
       float x = 0.f;
-      if (v < rows && c < P.ncols)
-        x = load_src(P.wsrc, smp * P.wsrc_stride_b + (int64_t)v * P.ld + c, P.wsrc_type);
+      if (v < rows && c < P.ncols) x = w_value(P, smp, v, c);
       ((float*)P.rec.W)[smp * P.rec.w_stride_b + q] = x;
     }
     return;
@@ -583,7 +593,7 @@ __device__ __forceinline__ float clip_value(float n, float C) {
 
 __global__ void __launch_bounds__(256) k_finish(const double2* __restrict__ partials, int32_t slots, float* n,
                                                 int accumulate, float* head, float* tail, float* c, float C,
-                                                int with_clip) {
+                                                int with_clip, double scale) {
   __shared__ double r0[256], r1[256];
   const int i = blockIdx.x, t = threadIdx.x;
   const double2* P = partials + (int64_t)i * slots;
@@ -604,11 +614,11 @@ __global__ void __launch_bounds__(256) k_finish(const double2* __restrict__ part
     __syncthreads();
   }
   if (t == 0) {
-    const double tot = r0[0] + r1[0];
+    const double tot = (r0[0] + r1[0]) * scale;
     const float nv = (float)(accumulate ? (double)n[i] + tot : tot);
     n[i] = nv;
-    if (head) head[i] = (float)r0[0];
-    if (tail) tail[i] = (float)r1[0];
+    if (head) head[i] = (float)(r0[0] * scale);
+    if (tail) tail[i] = (float)(r1[0] * scale);
     if (with_clip) c[i] = clip_value(nv, C);
   }
 }
@@ -686,9 +696,9 @@ hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode
 }
 
 hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, float* n, int accumulate, float* head,
-                         float* tail, float* c, float C, int with_clip, hipStream_t s) {
+                         float* tail, float* c, float C, int with_clip, double scale, hipStream_t s) {
   hipLaunchKernelGGL(k_finish, dim3(B), dim3(256), 0, s, partials, slots, n, accumulate, head, tail, c, C,
-                     with_clip);
+                     with_clip, scale);
   return hipGetLastError();
 }
 

@@ -62,12 +62,13 @@ class RandomizedClipping:
 
     or ``rc.step(losses, optimizer)`` for the last four lines.
 
-    estimator: "hutch" (k columns), "hutchpp" (budget k) or "exact".
+    estimator: "hutch" (k Gaussian columns), "hutch_sign" (k +-1 columns stored
+    as bits), "hutchpp" (budget k) or "exact".
     norm_dtype: element type handed to the norm path (bfloat16 or float32;
     default: the activations' own). Widths must suit that type (multiples of
     8 for bfloat16, 4 for float32).
     keep_layers: keep the (A, G, P) triples of the last step in
-    ``last_layers`` (P is None for the other estimators).
+    ``last_layers`` (P is the sign words for "hutch_sign", None for "exact").
     timer: an optional sample_grad_norms_amd.KernelTimer given to the grouped
     Hutchinson calls (per-launch times of the norm path).
     """
@@ -76,8 +77,8 @@ class RandomizedClipping:
                  estimator: str = "hutch", norm_dtype: Optional[torch.dtype] = None, seed: int = 0,
                  projection: ProjectionFn = gaussian_projection, keep_layers: bool = False,
                  timer: Optional["dp.KernelTimer"] = None):
-        if estimator not in ("hutch", "hutchpp", "exact"):
-            raise ValueError("estimator must be 'hutch', 'hutchpp' or 'exact'")
+        if estimator not in ("hutch", "hutch_sign", "hutchpp", "exact"):
+            raise ValueError("estimator must be 'hutch', 'hutch_sign', 'hutchpp' or 'exact'")
         if not C > 0:
             raise ValueError("C must be positive")
         self.C, self.sigma, self.k = float(C), float(noise_multiplier), int(k)
@@ -160,13 +161,20 @@ class RandomizedClipping:
         gen = self._generator(device)
         n = torch.zeros(B, dtype=torch.float32, device=device)
         used = []
-        if self.estimator == "hutch":
-            triples = [(A, G, self.projection(G.shape[2], self.k, A.dtype, device, gen)) for (A, G) in layers]
+        if self.estimator in ("hutch", "hutch_sign"):
+            if self.estimator == "hutch":
+                triples = [(A, G, self.projection(G.shape[2], self.k, A.dtype, device, gen)) for (A, G) in layers]
+            else:
+                triples = [(A, G, dp.random_signs(G.shape[2], self.k, device=device, generator=gen))
+                           for (A, G) in layers]
             # one grouped call per sequence length (a module applied u times has u T rows)
             lengths = sorted({A.shape[1] for (A, _, _) in triples})
             for j, T in enumerate(lengths):
-                dp.hutch_grouped([t for t in triples if t[0].shape[1] == T], out=n, accumulate=j > 0,
-                                 timer=self.timer)
+                part = [t for t in triples if t[0].shape[1] == T]
+                if self.estimator == "hutch":
+                    dp.hutch_grouped(part, out=n, accumulate=j > 0, timer=self.timer)
+                else:
+                    dp.hutch_sign_grouped(part, self.k, out=n, accumulate=j > 0)
             used = triples
         else:
             for (A, G) in layers:

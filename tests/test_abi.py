@@ -182,6 +182,23 @@ def test_clip_factor_checks(lib):
     assert lib.dpnorm_clip_factors(N_ADDR + 2, 4, 1.0, N_ADDR + 64, None) == _lib.ERR_ALIGN
 
 
+def test_hutch_sign_checks(lib):
+    def call(S=P_ADDR, k=8, A=A_ADDR, ws_bytes=None, acc=0):
+        if ws_bytes is None:
+            ws_bytes = ws_query(lib, _lib.BF16, 2, 100, 64, 32, k)[1] - 1   # one byte short: never launches
+        return lib.dpnorm_hutch_sign(A, G_ADDR, S, _lib.BF16, 2, 100, 64, 32, k, N_ADDR, acc, WS_ADDR, ws_bytes, None)
+    assert call() == _lib.ERR_WORKSPACE
+    assert call(S=None) == _lib.ERR_NULL
+    assert call(S=P_ADDR + 2) == _lib.ERR_ALIGN        # words need 4-byte alignment
+    assert call(S=P_ADDR + 4) == _lib.ERR_WORKSPACE    # 4-byte aligned is enough
+    assert call(k=0, ws_bytes=1 << 30) == _lib.ERR_SIZE
+    assert call(k=65, ws_bytes=1 << 30) == _lib.ERR_SIZE
+    assert call(acc=2, ws_bytes=1 << 30) == _lib.ERR_VALUE
+    arr = (_lib.Layer * 1)(_lib.Layer(A_ADDR, G_ADDR, None, 64, 32))
+    st = lib.dpnorm_hutch_sign_grouped(arr, 1, _lib.BF16, 2, 100, 8, N_ADDR, 0, None, 1.0, WS_ADDR, 1 << 30, None)
+    assert st == _lib.ERR_NULL
+
+
 def test_read_probe_checks(lib):
     assert lib.dpnorm_read_probe(None, 16384, None) == _lib.ERR_NULL
     for bad in (0, -16384, 16383, 16384 + 8):

@@ -170,6 +170,22 @@ def test_bf16_llama_step_hutch_parity_and_update():
         assert torch.isfinite(p).all() and not torch.equal(p, p0)
 
 
+def test_sign_estimator_in_the_step():
+    from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+    shape = dict(layers=1, dim=64, heads=2, kv_heads=1, hidden=128, vocab=32)
+    model = lb.build(81, device=dev(), dtype=torch.bfloat16, **shape)
+    x, y = lb.batch(82, 3, 40, 64, 32, device=dev(), dtype=torch.bfloat16)
+    rc = RandomizedClipping(model, C=1.0, noise_multiplier=0.0, estimator="hutch_sign", k=32, keep_layers=True)
+    with rc.capture():
+        losses = lb.per_sample_loss(model(x), y)
+    n, _ = rc.clip_factors(losses)
+    torch.cuda.synchronize()
+    want = oracle.layer_sum([oracle.hutch_sign(A, G, S, 32) for (A, G, S) in rc.last_layers])
+    err = rel(n.cpu(), want)
+    print(f"sign estimator in the step: max rel err {err.max():.2e}", flush=True)
+    assert np.all(err <= 1e-3)
+
+
 def test_other_estimators_run_in_the_step():
     from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
     shape = dict(layers=1, dim=64, heads=2, kv_heads=1, hidden=128, vocab=32)
