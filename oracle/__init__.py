@@ -18,7 +18,9 @@ from .reference import (  # noqa: F401
     hutchpp_sample,
     hutchpp_split,
     layer_sum,
+    norms_routed,
     orthonormal_basis,
+    routes_exact,
     to_f64,
     unpack_signs,
 )

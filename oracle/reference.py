@@ -151,6 +151,29 @@ def hutch_sign(A, G, S_bits, k: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Route between the exact norm and the estimate [RC-note 实验关键数据: full
+#  fine-tuning and LoRA; 研究背景与动机: the exact norm is what the estimate
+#  replaces]. Reading: a layer whose narrow side min(d, p) is at most k gets
+#  its exact norm (a k-column estimate would cost as much); the others get the
+#  Hutchinson estimate with their P.
+# --------------------------------------------------------------------------
+
+def routes_exact(d: int, p: int, k: int) -> bool:
+    return min(int(d), int(p)) <= int(k)
+
+
+def norms_routed(layers, k: int):
+    """Per-sample sum over (A, G, P) layers of exact_explicit (routed layers)
+    or hutch (the others); returns (n, routes) with routes 1 for exact."""
+    parts, routes = [], []
+    for (A, G, P) in layers:
+        exact = routes_exact(A.shape[-1], G.shape[-1], k)
+        parts.append(exact_explicit(A, G) if exact else hutch(A, G, P))
+        routes.append(1 if exact else 0)
+    return layer_sum(parts), routes
+
+
+# --------------------------------------------------------------------------
 # Hutch++ [RC-note 关键设计 › Hutch++ 头-尾分解的低误差变体;
 #          RC-nl Kernmechanisme item 2]
 # --------------------------------------------------------------------------
