@@ -232,6 +232,42 @@ def sign_projection_stack(args, layers):
             "projection_bytes_bf16": sum(P.numel() * 2 for (_, _, P) in layers)}
 
 
+def lora_stack(args):
+    """LoRA factors (rank 16) of every projection of the Llama-3.2-1B-shaped
+    stack (224 factors, B=4, T=4096): the routed call (exact norms, since
+    every factor's narrow side is 16 <= k = 32) against the Hutchinson
+    estimate with k = 32 on the same factors and against dpnorm_exact called
+    per factor."""
+    import torch
+    import sample_grad_norms_amd as dp
+    import workloads
+    dev = torch.device("cuda:0")
+    B, T, k = 4, 4096, 32
+    layers = workloads.lora_stack(device=dev, B=B, T=T, k=k)
+    inputs = {}
+    for (A, G, _) in layers:
+        inputs[A.data_ptr()] = A.numel() * A.element_size()
+        inputs[G.data_ptr()] = G.numel() * G.element_size()
+    alg = sum(inputs.values())
+    n = torch.empty(B, dtype=torch.float32, device=dev)
+    routed = [(A, G, None) for (A, G, _) in layers]
+    ms_routed = timed(lambda: dp.norms_routed(routed, k, out=n), args.steps, args.warmup)
+    ms_hutch = timed(lambda: dp.hutch_grouped(layers, out=n), args.steps, args.warmup)
+    ws = torch.empty(max(dp.exact_workspace(torch.bfloat16, B, T, A.shape[2], G.shape[2]) for (A, G, _) in layers),
+                     dtype=torch.uint8, device=dev)
+
+    def exact_each():
+        for j, (A, G, _) in enumerate(layers):
+            dp.exact(A, G, out=n, accumulate=j > 0, workspace=ws)
+    ms_exact = timed(exact_each, max(2, args.steps // 4), 1)
+    out = {"factors": len(layers), "rank": 16, "algorithmic_bytes": alg,
+           "routed_exact_ms": ms_routed, "routed_samples_tokens_per_s": B * T / (ms_routed * 1e-3),
+           "routed_hbm_gbs": alg / (ms_routed * 1e-3) / 1e9, "hutch_k32_ms": ms_hutch,
+           "exact_call_per_factor_ms": ms_exact}
+    del layers, routed
+    return out
+
+
 def extras(args):
     """Other workloads: single-layer Hutchinson, Hutch++ and the exact
     comparator, each timed the same way."""
@@ -404,6 +440,7 @@ def main():
         rec["extras"] = {"hbm_calibration": hbm_calibration(dev),
                          "llama_shared_inputs_B4_T4096_k32": shared_input_stack(args),
                          "llama_stack_sign_projections_B4_T4096_k32": sign_projection_stack(args, layers),
+                         "lora_r16_llama1b_B4_T4096": lora_stack(args),
                          "dpsgd_rc_step_llama1b_width_2layers_B4_T2048": dpsgd_rc_step(args)}
         rec["extras"].update(extras(args))
     if not args.no_cpu_baseline:

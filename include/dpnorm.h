@@ -192,6 +192,24 @@ dpnorm_status dpnorm_hutch_sign_grouped(const dpnorm_layer* layers, int64_t L, d
                                         float* c, float C, void* ws, size_t ws_bytes,
                                         hipStream_t stream);
 
+/* Per-layer route between the exact norm and the Hutchinson estimate, summed
+ * per sample (note: 实验关键数据 covers full fine-tuning and LoRA; in a LoRA
+ * factor one side of W = A^T G is the rank r, far below the p and d of the
+ * base layer). A layer whose narrow side min(d, p) is at most k gets its exact
+ * norm ||A_i^T G_i||_F^2: contracting W over that side costs no more than a
+ * k-column estimate (both read A and G once), so nothing is gained by
+ * estimating it. Its P is not read and may be NULL. Every other layer gets
+ * the Hutchinson estimate with its P [p][k], as in dpnorm_hutch_grouped.
+ * n[i] (+)= sum over layers; c as in dpnorm_hutch_grouped. If routes is not
+ * NULL it is a host array of L entries that receives 1 for an exact layer and
+ * 0 for an estimated one. Workspace from dpnorm_norms_routed_workspace (same
+ * descriptors). Errors as dpnorm_hutch_grouped. */
+dpnorm_status dpnorm_norms_routed_workspace(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
+                                            int64_t B, int64_t T, int64_t k, size_t* bytes);
+dpnorm_status dpnorm_norms_routed(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                  int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
+                                  int32_t* routes, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Hutch++ estimate of one layer with budget k (note: 关键设计 › Hutch++;
  * summary: Kernmechanisme item 2). With (m_s, m_t) from
  * dpnorm_hutchpp_split(k), S is [p][m_s] (sketch, any scale; N(0,1)

@@ -279,6 +279,60 @@ def hutch_sign_grouped(layers, k: int, out: Optional[torch.Tensor] = None, accum
     return (n, c) if c is not None else n
 
 
+def routes_exact(d: int, p: int, k: int) -> bool:
+    """True when norms_routed computes a layer's exact norm (min(d, p) <= k)."""
+    return min(d, p) <= k
+
+
+def norms_routed(layers, k: int, out: Optional[torch.Tensor] = None, accumulate: bool = False,
+                 C_clip: Optional[float] = None, clip_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, return_routes: bool = False):
+    """Per-sample sum over layers of the exact norm (layers with min(d, p) <= k)
+    or the Hutchinson estimate (the others), dpnorm_norms_routed. ``layers``
+    are (A, G, P) triples; P may be None for exactly routed layers, else it
+    is [p][k] of the inputs' type. Returns n, (n, c) with C_clip, and the
+    per-layer routes (1 exact, 0 estimated) last when return_routes."""
+    if len(layers) == 0:
+        raise ValueError("at least one layer is needed")
+    A0 = layers[0][0]
+    _need(A0, "A", 3)
+    dtype, device = A0.dtype, A0.device
+    B, T = A0.shape[0], A0.shape[1]
+    arr = (_lib.Layer * len(layers))()
+    for j, (A, G, P) in enumerate(layers):
+        _need(A, f"layers[{j}].A", 3, dtype)
+        _need(G, f"layers[{j}].G", 3, dtype)
+        if A.shape[:2] != (B, T) or G.shape[:2] != (B, T):
+            raise ValueError(f"layers[{j}]: A and G must be [B={B}][T={T}][*]")
+        if P is None:
+            if not routes_exact(A.shape[2], G.shape[2], k):
+                raise ValueError(f"layers[{j}]: P is needed (min(d, p) > k)")
+        else:
+            _need(P, f"layers[{j}].P", 2, dtype)
+            if tuple(P.shape) != (G.shape[2], k):
+                raise ValueError(f"layers[{j}]: P must be [p={G.shape[2]}][k={k}]")
+        arr[j] = _lib.Layer(A.data_ptr(), G.data_ptr(), P.data_ptr() if P is not None else None, A.shape[2],
+                            G.shape[2])
+    L = lib()
+    nbytes = C.c_size_t(0)
+    _check(L.dpnorm_norms_routed_workspace(arr, len(layers), _code(dtype), B, T, k, C.byref(nbytes)),
+           "dpnorm_norms_routed_workspace")
+    n = _out(out, B, device, accumulate)
+    c = None
+    if C_clip is not None:
+        c = _out(clip_out, B, device, False, "clip_out") if clip_out is not None else torch.empty_like(n)
+    ws, wsp = _given_workspace(workspace, nbytes.value, device)
+    routes = (C.c_int32 * len(layers))()
+    _check(L.dpnorm_norms_routed(arr, len(layers), _code(dtype), B, T, k, n.data_ptr(), int(accumulate),
+                                 c.data_ptr() if c is not None else None,
+                                 float(C_clip) if C_clip is not None else 1.0, routes, wsp, nbytes.value,
+                                 _stream(device)), "dpnorm_norms_routed")
+    res = (n, c) if c is not None else (n,)
+    if return_routes:
+        res = res + (list(routes),)
+    return res if len(res) > 1 else res[0]
+
+
 def read_probe(buf: torch.Tensor) -> None:
     """Calibration: stream the whole of ``buf`` (a contiguous GPU tensor whose
     size is a multiple of 16384 bytes) once with the stage kernels' direct

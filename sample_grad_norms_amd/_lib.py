@@ -47,6 +47,10 @@ SIGNATURES = {
                           C.c_int),
     "dpnorm_hutch_sign_grouped": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32,
                                    _vp, _sz, _vp], C.c_int),
+    "dpnorm_norms_routed_workspace": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, C.POINTER(_sz)],
+                                      C.c_int),
+    "dpnorm_norms_routed": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32, _vp,
+                             _vp, _sz, _vp], C.c_int),
     "dpnorm_hutch_workspace": ([C.c_int, _i64, _i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "dpnorm_hutch_grouped_workspace": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "dpnorm_hutch": ([_vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _sz, _vp], C.c_int),

@@ -378,11 +378,24 @@ struct HutchCall {
   size_t bytes = 0;
 };
 
-// fuse: layers that share A (same pointer and d) share one stage-2 pass.
-// sign: each layer's P is bit-packed +-1 ([p][ceil(k/32)] 32-bit words); the
-// 1/sqrt(k) scale of the entries is applied as 1/k on the finished sums.
+// Kinds of Hutchinson call:
+//  HUTCH_DENSE : each layer's P is [p][k] of the call's element type;
+//  HUTCH_SIGN  : each layer's P is bit-packed +-1 ([p][ceil(k/32)] 32-bit
+//                words); the 1/sqrt(k) of the entries is applied as 1/k on
+//                the finished sums;
+//  HUTCH_ROUTED: as DENSE, except that a layer whose narrow side min(d, p) is
+//                at most k gets its exact norm: that side is projected by the
+//                identity, so the two stages contract W = A^T G over it (A and
+//                G swap roles when d is the narrow side); P is not read there.
+enum HutchKind { HUTCH_DENSE = 0, HUTCH_SIGN = 1, HUTCH_ROUTED = 2 };
+
+bool routed_exact(int64_t d, int64_t p, int64_t k) { return std::min(d, p) <= k; }
+
+// fuse: layers that share their streamed input (same pointer and width)
+// share one stage-2 pass.
 dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
-                          bool need_ptrs, bool fuse, bool sign, HutchCall& hc) {
+                          bool need_ptrs, bool fuse, HutchKind kind, HutchCall& hc) {
+  const bool sign = kind == HUTCH_SIGN;
   if (!layers) return DPNORM_ERR_NULL;
   if (!dtype_ok(dt)) return DPNORM_ERR_DTYPE;
   if (L < 1 || L > (1 << 20)) return DPNORM_ERR_SIZE;
@@ -393,21 +406,35 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
     const dpnorm_layer& y = layers[l];
     const dpnorm_status st = check_dims(dt, B, T, y.d, y.p);
     if (st != DPNORM_OK) return st;
+    const bool exact = kind == HUTCH_ROUTED && routed_exact(y.d, y.p, k);
     if (need_ptrs) {
-      if (!y.A || !y.G || !y.P) return DPNORM_ERR_NULL;
-      if (!aligned(y.A, 16) || !aligned(y.G, 16) || !aligned(y.P, sign ? 4 : esize(dt))) return DPNORM_ERR_ALIGN;
+      if (!y.A || !y.G || (!exact && !y.P)) return DPNORM_ERR_NULL;
+      if (!aligned(y.A, 16) || !aligned(y.G, 16)) return DPNORM_ERR_ALIGN;
+      if (!exact && !aligned(y.P, sign ? 4 : esize(dt))) return DPNORM_ERR_ALIGN;
     }
     PassLayer& pl = hc.layers[l];
-    pl.X1 = y.G;
-    pl.X2 = y.A;
-    pl.w1 = y.p;
-    pl.w2 = y.d;
-    pl.wsrc = y.P;
-    pl.wsrc_type = sign ? SRC_SIGN : (dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32);
-    pl.ld = sign ? (k + 31) / 32 : k;
-    pl.ncols = (int)k;
+    if (exact) {
+      const bool swap = y.d < y.p;  // project the narrow side
+      pl.X1 = swap ? y.A : y.G;
+      pl.X2 = swap ? y.G : y.A;
+      pl.w1 = swap ? y.d : y.p;
+      pl.w2 = swap ? y.p : y.d;
+      pl.wsrc = nullptr;
+      pl.wsrc_type = SRC_IDENTITY;
+      pl.ld = 0;
+      pl.ncols = (int)pl.w1;
+    } else {
+      pl.X1 = y.G;
+      pl.X2 = y.A;
+      pl.w1 = y.p;
+      pl.w2 = y.d;
+      pl.wsrc = y.P;
+      pl.wsrc_type = sign ? SRC_SIGN : (dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32);
+      pl.ld = sign ? (k + 31) / 32 : k;
+      pl.ncols = (int)k;
+    }
     items1 += B * ((T + kRowsK1 - 1) / kRowsK1);
-    items2 += B * ((y.d + kColsK2F32 - 1) / kColsK2F32) * 64;
+    items2 += B * ((pl.w2 + kColsK2F32 - 1) / kColsK2F32) * 64;
   }
   if (items1 >= ((int64_t)1 << 31) || items2 >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;
   PassPlan& p = hc.plan;
@@ -426,15 +453,16 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
 
 dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T, int64_t k,
                          float* n, int accumulate, float* c, float C, void* ws, size_t ws_bytes, hipStream_t stream,
-                         dpnorm_trace* trace, bool sign = false) {
+                         dpnorm_trace* trace, HutchKind kind = HUTCH_DENSE, int32_t* routes = nullptr) {
+  const bool sign = kind == HUTCH_SIGN;
   HutchCall hc;
-  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, sign, hc);
+  dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, kind, hc);
   if (st != DPNORM_OK) return st;
   // A workspace sized without knowing which layers share A (a query with
   // NULL pointers) may be too small for the fused plan: run unfused then.
   if (ws_bytes < hc.bytes) {
     HutchCall plain;
-    if (build_hutch(layers, L, dt, B, T, k, true, false, sign, plain) == DPNORM_OK && ws_bytes >= plain.bytes)
+    if (build_hutch(layers, L, dt, B, T, k, true, false, kind, plain) == DPNORM_OK && ws_bytes >= plain.bytes)
       hc = std::move(plain);
   }
   if (!n) return DPNORM_ERR_NULL;
@@ -454,9 +482,11 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
     const dpnorm_layer& y = layers[l];
     const size_t sa = (size_t)B * T * y.d * e, sg = (size_t)B * T * y.p * e;
     const size_t sp = sign ? (size_t)y.p * ((k + 31) / 32) * 4 : (size_t)y.p * k * e;
+    const bool reads_P = !(kind == HUTCH_ROUTED && routed_exact(y.d, y.p, k));
     for (const float* o : {(const float*)n, (const float*)c}) {
       if (!o) continue;
-      if (overlaps(o, nb, y.A, sa) || overlaps(o, nb, y.G, sg) || overlaps(o, nb, y.P, sp)) return DPNORM_ERR_VALUE;
+      if (overlaps(o, nb, y.A, sa) || overlaps(o, nb, y.G, sg) || (reads_P && overlaps(o, nb, y.P, sp)))
+        return DPNORM_ERR_VALUE;
     }
   }
   if (overlaps(n, nb, ws, hc.bytes) || (c && overlaps(c, nb, ws, hc.bytes))) return DPNORM_ERR_VALUE;
@@ -467,6 +497,8 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
     if (trace->capacity < need + 1) return DPNORM_ERR_SIZE;
   }
 
+  if (routes)
+    for (int64_t l = 0; l < L; ++l) routes[l] = kind == HUTCH_ROUTED && routed_exact(layers[l].d, layers[l].p, k) ? 1 : 0;
   Tracer tr;
   tr.t = trace;
   tr.s = stream;
@@ -611,7 +643,7 @@ dpnorm_status dpnorm_hutch_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int6
   y.d = d;
   y.p = p;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, true, false, hc);
+  const dpnorm_status st = build_hutch(&y, 1, dt, B, T, k, false, true, HUTCH_DENSE, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;
@@ -621,7 +653,7 @@ dpnorm_status dpnorm_hutch_grouped_workspace(const dpnorm_layer* layers, int64_t
                                              int64_t T, int64_t k, size_t* bytes) {
   if (!bytes) return DPNORM_ERR_NULL;
   HutchCall hc;
-  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, false, hc);
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, HUTCH_DENSE, hc);
   if (st != DPNORM_OK) return st;
   *bytes = hc.bytes;
   return DPNORM_OK;
@@ -661,13 +693,29 @@ dpnorm_status dpnorm_hutch_sign(const void* A, const void* G, const uint32_t* S_
   y.P = S_bits;
   y.d = d;
   y.p = p;
-  return hutch_impl(&y, 1, dt, B, T, k, n, accumulate, nullptr, 1.f, ws, ws_bytes, stream, nullptr, true);
+  return hutch_impl(&y, 1, dt, B, T, k, n, accumulate, nullptr, 1.f, ws, ws_bytes, stream, nullptr, HUTCH_SIGN);
 }
 
 dpnorm_status dpnorm_hutch_sign_grouped(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T,
                                         int64_t k, float* n, int accumulate, float* c, float C, void* ws,
                                         size_t ws_bytes, hipStream_t stream) {
-  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, nullptr, true);
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, nullptr, HUTCH_SIGN);
+}
+
+dpnorm_status dpnorm_norms_routed_workspace(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                            int64_t T, int64_t k, size_t* bytes) {
+  if (!bytes) return DPNORM_ERR_NULL;
+  HutchCall hc;
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, false, true, HUTCH_ROUTED, hc);
+  if (st != DPNORM_OK) return st;
+  *bytes = hc.bytes;
+  return DPNORM_OK;
+}
+
+dpnorm_status dpnorm_norms_routed(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B, int64_t T,
+                                  int64_t k, float* n, int accumulate, float* c, float C, int32_t* routes, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, nullptr, HUTCH_ROUTED, routes);
 }
 
 dpnorm_status dpnorm_hutchpp_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64_t p, int64_t k,

@@ -21,7 +21,8 @@ constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 1024;  // elements of a Y tile per split-T reduction work group
 constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
 
-enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1, SRC_SIGN = 2 };  // SIGN: bit-packed +-1, ld in 32-bit words
+// SIGN: bit-packed +-1, ld in 32-bit words; IDENTITY: W = I (no source array)
+enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1, SRC_SIGN = 2, SRC_IDENTITY = 3 };
 
 // Device-side description of one layer (written by the prepare kernel).
 struct LayerRec {

@@ -33,7 +33,9 @@ __device__ __forceinline__ float load_src(const void* p, int64_t idx, int type) 
 // Element (v, c) of sample smp's W source. Sign sources hold one bit per
 // entry, 32 columns to a word (bit c % 32 of word c / 32 of row v): 0 is +1,
 // 1 is -1; the 1/sqrt(k) scale is applied to the finished sums instead.
+// The identity source projects a narrow side onto itself (exact norms).
 __device__ __forceinline__ float w_value(const PrepLayer& P, int smp, int v, int c) {
+  if (P.wsrc_type == SRC_IDENTITY) return v == c ? 1.f : 0.f;
   const int64_t row = smp * P.wsrc_stride_b + (int64_t)v * P.ld;
   if (P.wsrc_type == SRC_SIGN) {
     const uint32_t word = ((const uint32_t*)P.wsrc)[row + (c >> 5)];

@@ -174,6 +174,33 @@ def shared_input_stack(device="cpu", B: int = 4, T: int = 4096, k: int = 32, lay
     return out
 
 
+def lora_stack(device="cpu", B: int = 4, T: int = 4096, k: int = 32, rank: int = 16,
+               layers: int = LLAMA_1B_LAYERS, dtype=torch.bfloat16):
+    """LoRA factors of every projection of the Llama-3.2-1B-shaped stack
+    (workload 7 of the seed rule). For a projection d -> p with rank-r
+    adapters x -> (x D) U, the per-sample gradients are those of the down
+    factor D (A = x [T][d], G [T][r]) and of the up factor U (A = x D [T][r],
+    G [T][p]). x is shared as in the real model (q, k, v read one input, gate
+    and up another); every tensor is s N(0,1) with s ~ U[0.5, 2]. Returns
+    (A, G, P) triples, down then up factor per projection, with a Gaussian
+    P ~ N(0, 1/k) [G's width][k] for each (an exact route does not read it)."""
+    out = []
+    for layer in range(layers):
+        inputs = {}
+        for j, (_, d, p) in enumerate(LLAMA_1B_PROJECTIONS):
+            index = 7 * layer + j
+            src = 7 * layer + LLAMA_1B_INPUT_OF[j]
+            sc = (0.5 + 1.5 * torch.rand(4, generator=_gen("cpu", seed_of(7, index, ROLE_SCALE)))).tolist()
+            if src not in inputs:
+                inputs[src] = gaussian((B, T, d), sc[0], seed_of(7, src, ROLE_A), device, dtype)
+            g_mid = gaussian((B, T, rank), sc[1], seed_of(7, index, ROLE_G), device, dtype)
+            a_mid = gaussian((B, T, rank), sc[2], seed_of(7, index, ROLE_S), device, dtype)
+            g_out = gaussian((B, T, p), sc[3], seed_of(7, index, ROLE_LOWRANK), device, dtype)
+            out.append((inputs[src], g_mid, projection(rank, k, seed_of(7, index, ROLE_P), device, dtype)))
+            out.append((a_mid, g_out, projection(p, k, seed_of(7, index, ROLE_P) + 50, device, dtype)))
+    return out
+
+
 def hutchpp_split(k: int) -> Tuple[int, int]:
     """Budget split used by the Hutch++ workloads: ceil(k/3) sketch columns,
     the same number of head columns, and k - 2 ceil(k/3) tail columns."""
