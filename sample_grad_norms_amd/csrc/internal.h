@@ -18,7 +18,7 @@ namespace dpn {
 constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
-constexpr int kYsumChunk = 1024;  // elements of a Y tile per split-T reduction work group
+constexpr int kYsumChunk = 256;   // elements of a Y tile per split-T reduction work group (one wave)
 constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
 
 // SIGN: bit-packed +-1, ld in 32-bit words; IDENTITY: W = I (no source array)

@@ -524,13 +524,14 @@ __global__ void __launch_bounds__(256) k_tcontract_f32(StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-T reduction: one work group per kYsumChunk elements of the Y tile of
-// a (layer, sample, column block). Each thread sums 4 consecutive elements
-// over the nsplit partial tiles in split order (fp64), then either squares
-// and reduces into its own partial slot (MODE_SQ) or stores Y (MODE_STORE).
+// Split-T reduction: one wave per kYsumChunk elements of the Y tile of a
+// (layer, sample, column block). Each lane sums 4 consecutive elements over
+// the nsplit partial tiles in split order (fp64; eight splits' loads are in
+// flight at a time), then either squares and reduces into the wave's own
+// partial slot (MODE_SQ) or stores Y (MODE_STORE).
 // ---------------------------------------------------------------------------
 template <int MODE>
-__global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_block, int ychunks) {
+__global__ void __launch_bounds__(64) k_ysum(StageArgs a, int NC, int cols_per_block, int ychunks) {
   const int blk = blockIdx.x / ychunks, chunk = blockIdx.x - blk * ychunks;
   const int4 it = a.items[(int64_t)blk * a.nsplit];
   const LayerRec* L = a.recs + it.x;
@@ -545,6 +546,7 @@ __global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_
   double s0 = 0.0, s1 = 0.0;
   if (e < nel) {  // nel is a multiple of 16, so all four elements are in the tile
     double y[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
     for (int ts = 0; ts < a.nsplit; ++ts) {
       const float4 v = ldg_f32x4(Yp + ts * tile + e);
       y[0] += (double)v.x;
@@ -565,19 +567,10 @@ __global__ void __launch_bounds__(256) k_ysum(StageArgs a, int NC, int cols_per_
     }
   }
   if (MODE == MODE_SQ) {
-    __shared__ double red[4][2];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     s0 = wave_sum(s0);
     s1 = wave_sum(s1);
-    if (lane == 0) {
-      red[wv][0] = s0;
-      red[wv][1] = s1;
-    }
-    __syncthreads();
     if (threadIdx.x == 0)
-      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub * ychunks + chunk] =
-          make_double2((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]),
-                       (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]));
+      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub * ychunks + chunk] = make_double2(s0, s1);
   }
 }
 
@@ -691,9 +684,9 @@ hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(blocks * ychunks);
   if (mode == MODE_SQ)
-    hipLaunchKernelGGL(k_ysum<MODE_SQ>, grid, dim3(256), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+    hipLaunchKernelGGL(k_ysum<MODE_SQ>, grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   else
-    hipLaunchKernelGGL(k_ysum<MODE_STORE>, grid, dim3(256), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+    hipLaunchKernelGGL(k_ysum<MODE_STORE>, grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   return hipGetLastError();
 }
 
