@@ -77,8 +77,11 @@ __device__ __forceinline__ uint4 pack8(const uint32_t b[8]) {
 // In-register transpose of an 8 x 8 block of bf16.
 // in[s] holds 8 consecutive elements (columns e = 0..7) of row s;
 // out[e] holds rows s = 0..7 of column e, row 0 in the low half of word 0.
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// Low halves (pack_lo16) or high halves (pack_hi16) of a and b as one word,
+// a's half in the low 16 bits: one v_perm_b32 each, whose result byte i is
+// byte sel_i of the eight bytes {a (0-3), b (4-7)}.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -116,6 +119,40 @@ __device__ __forceinline__ int xcd_item(uint32_t b, uint32_t n) {
   const uint32_t x = b & 7u, j = b >> 3;
   const uint32_t per = n >> 3, rem = n & 7u;
   return (int)(x * per + (x < rem ? x : rem) + j);
+}
+
+// ---------------------------------------------------------------------------
+// Direct global-to-LDS streaming (global_load_lds_dwordx4), shared by the
+// stage kernels, the exact comparator and the calibration stream.
+// ---------------------------------------------------------------------------
+// s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt at max).
+#define DPN_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
+
+// 16 bytes per lane from global memory to LDS at lds_addr + 16 * lane
+// (lds_addr wave-uniform), non-temporal (dma16_stream) or cached (dma16).
+// The loads are issued from inline assembly so that the compiler adds no
+// waits for them: the kernels place their own vector-memory waits. M0
+// carries the LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16_stream(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+// Work-group barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(after * P) for after in 0..2: at most `after` later
+// stages' loads (P per stage) still outstanding.
+template <int P>
+__device__ __forceinline__ void wait_after(int after) {
+  if (after >= 2) DPN_WAIT_VMCNT(2 * P);
+  else if (after == 1) DPN_WAIT_VMCNT(P);
+  else DPN_WAIT_VMCNT(0);
 }
 
 }  // namespace dpn

@@ -77,6 +77,9 @@ struct PassPlan {
   size_t off_recs = 0, off_items1 = 0, off_items2 = 0, off_partials = 0;
   std::vector<size_t> off_W;
   std::vector<int> k1_begin, n1, n_pack, group_of, jb0;  // per layer
+  // prepare-table entries: (layer, group) pairs; a layer alone in its group
+  // carries the group too, a group of several layers has an entry of its own
+  std::vector<std::pair<int, int>> entries;
   std::vector<PassGroup> groups;
   std::vector<int> class_ncb, class_begin, class_end;    // stage-2 item ranges, one per group width
   int64_t total1 = 0, total2 = 0;
@@ -189,7 +192,14 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
       pl.class_end.push_back((int)pl.total2);
     }
   }
-  pl.off_recs = bump.take(sizeof(LayerRec) * (nl + ng));
+  pl.entries.clear();
+  for (int l = 0; l < nl; ++l) {
+    const int gi = pl.group_of[l];
+    pl.entries.push_back({l, pl.groups[gi].members.size() == 1 ? gi : -1});
+  }
+  for (int gi = 0; gi < ng; ++gi)
+    if (pl.groups[gi].members.size() > 1) pl.entries.push_back({-1, gi});
+  pl.off_recs = bump.take(sizeof(LayerRec) * pl.entries.size());
   pl.off_items1 = bump.take(sizeof(int4) * pl.total1);
   pl.off_items2 = bump.take(sizeof(int4) * pl.total2);
   pl.off_partials = bump.take(sizeof(double2) * pl.B * pl.slots);
@@ -203,7 +213,8 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
 }
 
 int pass_launches(const PassPlan& pl, int nl) {
-  const int entries = nl + (int)pl.groups.size();
+  (void)nl;
+  const int entries = (int)pl.entries.size();
   const int classes = (int)pl.class_ncb.size();
   return (entries + kPrepChunk - 1) / kPrepChunk + 1 + classes * (pl.needs_ysum() ? 2 : 1);
 }
@@ -230,13 +241,10 @@ struct Tracer {
     if (e_ != hipSuccess) return e_;               \
   } while (0)
 
-// Prepare-table entries: entry e < nl is layer e (stage 1), entry nl + g is
-// stage-2 group g; the record of entry e is recs[e].
+// The record of prepare-table entry e (pl.entries) is recs[e].
 hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, hipStream_t s,
                     Tracer& tr) {
-  const int nl = (int)L.size();
-  const int ng = (int)pl.groups.size();
-  const int entries = nl + ng;
+  const int entries = (int)pl.entries.size();
   LayerRec* recs = (LayerRec*)(base + pl.off_recs);
   int4* items1 = (int4*)(base + pl.off_items1);
   int4* items2 = (int4*)(base + pl.off_items2);
@@ -258,18 +266,19 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
       PrepLayer& P = a.L[j];
       LayerRec& R = P.rec;
       R.split = 1 << 30;
-      if (e < nl) {  // stage-1 projection
-        const PassLayer& in = L[e];
-        const PassGroup& g = pl.groups[pl.group_of[e]];
+      const int le = pl.entries[e].first, ge = pl.entries[e].second;
+      if (le >= 0) {  // stage-1 projection
+        const PassLayer& in = L[le];
+        const PassGroup& g = pl.groups[pl.group_of[le]];
         R.X1 = in.X1;
-        R.W = base + pl.off_W[e];
+        R.W = base + pl.off_W[le];
         R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
         R.w1 = (int32_t)in.w1;
         if (pl.bf16) {
-          R.V = (uint4*)(base + g.off_V) + (size_t)pl.jb0[e] * 2 * 64;
+          R.V = (uint4*)(base + g.off_V) + (size_t)pl.jb0[le] * 2 * 64;
           R.vstride = g.ncb * 2 * 64;
         } else {
-          R.V = (float*)(base + g.off_V) + (size_t)pl.jb0[e] * 16;
+          R.V = (float*)(base + g.off_V) + (size_t)pl.jb0[le] * 16;
           R.vstride = 16 * g.ncb;
         }
         P.wsrc = in.wsrc;
@@ -278,11 +287,12 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
         P.ld = (int32_t)in.ld;
         P.ncols = in.ncols;
         P.nsamples = in.nsamples;
-        P.n_pack = pl.n_pack[e];
-        P.k1_begin = pl.k1_begin[e];
-        P.n1 = pl.n1[e];
-      } else {  // stage-2 group
-        const PassGroup& g = pl.groups[e - nl];
+        P.n_pack = pl.n_pack[le];
+        P.k1_begin = pl.k1_begin[le];
+        P.n1 = pl.n1[le];
+      }
+      if (ge >= 0) {  // stage-2 group (V is the group's whole V, at offset 0 for a lone layer)
+        const PassGroup& g = pl.groups[ge];
         const PassLayer& in = L[g.members[0]];
         R.X2 = in.X2;
         R.V = base + g.off_V;

@@ -11,7 +11,6 @@ namespace dpn {
 constexpr int kProbeStage = 16384;      // bytes per stage
 constexpr int kProbeStages = 64;        // stages per work group (1 MB)
 
-#define DPN_PROBE_WAIT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
 
 __global__ void __launch_bounds__(256) k_read_probe(const unsigned char* __restrict__ buf, int64_t nstages) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kProbeStage];
@@ -24,19 +23,14 @@ __global__ void __launch_bounds__(256) k_read_probe(const unsigned char* __restr
     const unsigned char* src = buf + (s0 + st) * kProbeStage + (wv * 4) * 1024 + lane * 16;
     const uint32_t dst = base + (uint32_t)((st & 3) * kProbeStage + wv * 4 * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src + j * 1024),
-                   "s"(__builtin_amdgcn_readfirstlane(dst + j * 1024))
-                   : "memory");
+    for (int j = 0; j < 4; ++j) dma16_stream(src + j * 1024, dst + j * 1024);
   };
   dma(0);
   dma(1);
   dma(2);
   for (int st = 0; st < nst; ++st) {
-    if (st + 2 < nst) DPN_PROBE_WAIT(8);
-    else if (st + 1 < nst) DPN_PROBE_WAIT(4);
-    else DPN_PROBE_WAIT(0);
-    asm volatile("s_barrier" ::: "memory");
+    wait_after<4>(min(2, nst - 1 - st));
+    block_barrier();
     dma(st + 3);
   }
 }

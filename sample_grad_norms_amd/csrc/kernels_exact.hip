@@ -29,45 +29,87 @@ struct ExactArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Explicit, bf16: one wave per 128 (d) x 128 (p) tile of W_i. Per 32-row chunk
-// a lane loads 8 rows of 8 consecutive columns of A and of G, transposes both
-// 8 x 8 blocks so T runs along the K slots, and issues the 64 MFMAs of the
-// tile; the next chunk's loads are in flight meanwhile.
+// Explicit, bf16: one work group per 256 (d) x 256 (p) tile of W_i, each wave
+// a 128 x 128 quarter (wave w: A columns 128 (w % 2), G columns 128 (w / 2)).
+// Every 32-row chunk of the tile's A and G columns (2 x 16 KB) is streamed
+// into LDS with direct global-to-LDS loads (four-slot ring, three chunks in
+// flight), so each A and G fragment is read from memory once for two waves.
+// A lane then reads 8 rows of its 8 consecutive columns of each operand from
+// LDS, transposes both 8 x 8 blocks so T runs along the MFMA K slots, and
+// issues the 64 MFMAs of its quarter. Rows past T and columns past d or p
+// load the last valid row / column and are zeroed after the LDS read.
+// Tiles are numbered with the A tile fastest, so the tiles one XCD takes (a
+// contiguous range) cover all of A for a few G tiles, and G is fetched from
+// HBM about once.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) k_exact_explicit_bf16(ExactArgs a) {
+constexpr int kXTile = 256;                       // tile edge along d and along p
+constexpr int kXRows = 32;                        // rows per chunk (one MFMA K step)
+constexpr int kXOpBytes = kXRows * kXTile * 2;    // one operand's chunk (16 KB)
+constexpr int kXBufs = 4;                         // LDS ring: three chunks in flight, one in use
+
+__global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
+  constexpr int kStage = 2 * kXOpBytes;           // A chunk, then G chunk
+  constexpr int kDma = kXOpBytes / 1024 / 4;      // 1 KB loads per wave per operand per chunk
+  constexpr int kP = 2 * kDma;                    // loads per wave per chunk
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kXBufs * kStage];
+  __shared__ double red[4];
   const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
   const int per_i = a.tu * a.tv;
   const int i = item / per_i, rem = item - i * per_i;
-  const int tu = rem / a.tv, tv = rem - tu * a.tv;
-  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const int tv = rem / a.tu, tu = rem - tv * a.tu;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
   const int T = a.T, d = a.d, p = a.p;
-  const int ua = 128 * tu + 8 * n, vb = 128 * tv + 8 * n;
-  const bool aok = ua < d, gok = vb < p;
-  const uint16_t* Ap = (const uint16_t*)a.A + (int64_t)i * T * d + ua;
-  const uint16_t* Gp = (const uint16_t*)a.G + (int64_t)i * T * p + vb;
-  const int nch = (T + 31) >> 5;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
+  // loads: instruction j of wave wv fills chunk rows 8 wv + 2 j + lane / 32,
+  // 16-byte unit lane % 32 of the tile's 256 columns (512 bytes per row).
+  // Rows past T load row T - 1 (zeroed after the LDS read); columns past d
+  // or p load the last valid column, and the W entries they make are left
+  // out of the sum below.
+  const int drow = 8 * wv + (lane >> 5);
+  const int acol = min(kXTile * tu + 8 * (lane & 31), d - 8);
+  const int gcol = min(kXTile * tv + 8 * (lane & 31), p - 8);
+  const uint16_t* As = (const uint16_t*)a.A + (int64_t)i * T * d + acol;
+  const uint16_t* Gs = (const uint16_t*)a.G + (int64_t)i * T * p + gcol;
+  const int nch = (T + kXRows - 1) / kXRows;
+  auto dma = [&](int c) {
+    if (c >= nch) return;
+    const uint32_t buf = lds_base + (uint32_t)((c % kXBufs) * kStage);
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+      int t = kXRows * c + drow + 2 * j;
+      t = t < T ? t : T - 1;
+      const uint32_t off = (uint32_t)((4 * wv + j) * 1024);
+      dma16_stream(As + (int64_t)t * d, buf + off);
+      dma16_stream(Gs + (int64_t)t * p, buf + kXOpBytes + off);
+    }
+  };
+
+  const int wa = wv & 1, wg = wv >> 1;
+  const int ao = (128 * wa + 8 * n) * 2, go = (128 * wg + 8 * n) * 2;  // byte offsets of this lane's columns
   f32x4_t acc[8][8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int f = 0; f < 8; ++f) acc[e][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  auto load = [&](int c, uint4 (&ra)[8], uint4 (&rg)[8]) {
+#pragma unroll
+  for (int c = 0; c < kXBufs - 1; ++c) dma(c);
+  for (int c = 0; c < nch; ++c) {
+    wait_after<kP>(min(kXBufs - 2, nch - 1 - c));
+    block_barrier();
+    dma(c + kXBufs - 1);
+    const unsigned char* buf = lds + (c % kXBufs) * kStage;
+    const int t0 = kXRows * c;
+    uint4 ra[8], rg[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int t = 32 * c + slot_row(g, s);
-      const bool tok = c < nch && t < T;
-      ra[s] = (tok && aok) ? ldg16(Ap + (int64_t)t * d) : z;
-      rg[s] = (tok && gok) ? ldg16(Gp + (int64_t)t * p) : z;
+      const int r = slot_row(g, s);
+      const uint4 xa = *(const uint4*)(buf + r * 512 + ao);
+      ra[s] = t0 + r < T ? xa : make_uint4(0, 0, 0, 0);  // A rows past T are zero
+      rg[s] = *(const uint4*)(buf + kXOpBytes + r * 512 + go);
     }
-  };
-  uint4 ra[8], rg[8];
-  load(0, ra, rg);
-  for (int c = 0; c < nch; ++c) {
-    uint4 na[8], ng[8];
-    load(c + 1, na, ng);
     uint4 oa[8], og[8];
     transpose8x8_bf16(ra, oa);
     transpose8x8_bf16(rg, og);
@@ -75,12 +117,10 @@ __global__ void __launch_bounds__(64) k_exact_explicit_bf16(ExactArgs a) {
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int f = 0; f < 8; ++f) acc[e][f] = mfma_bf16(oa[e], og[f], acc[e][f]);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      ra[s] = na[s];
-      rg[s] = ng[s];
-    }
   }
+  // acc[e][f] lane (n, g), register r: W[u][v] with u = column 128 wa + 8 (4 g + r) + e
+  // of the tile's A columns and v = 128 wg + 8 n + f of its G columns
+  const int u0 = kXTile * tu + 128 * wa, v0 = kXTile * tv + 128 * wg;
   double ss = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -89,10 +129,12 @@ __global__ void __launch_bounds__(64) k_exact_explicit_bf16(ExactArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const double y = (double)acc[e][f][r];
-        ss += y * y;
+        if (u0 + 8 * (4 * g + r) + e < d && v0 + 8 * n + f < p) ss += y * y;
       }
   ss = wave_sum(ss);
-  if (lane == 0) a.partials[(int64_t)i * a.slots + rem] = make_double2(ss, 0.0);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) a.partials[(int64_t)i * a.slots + rem] = make_double2((red[0] + red[1]) + (red[2] + red[3]), 0.0);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,7 +333,7 @@ void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t&
     tv = tu;
     slots = tu * (tu + 1) / 2;
   } else {
-    const int64_t e = bf16 ? 128 : 64;
+    const int64_t e = bf16 ? kXTile : 64;
     tu = (int32_t)((d + e - 1) / e);
     tv = (int32_t)((p + e - 1) / e);
     slots = tu * tv;
@@ -314,7 +356,7 @@ hipError_t launch_exact(const void* A, const void* G, bool bf16, bool gram, int3
     if (bf16) hipLaunchKernelGGL(k_exact_gram_bf16, dim3(a.n_items), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_exact_gram_f32, dim3(a.n_items), dim3(256), 0, s, a);
   } else {
-    if (bf16) hipLaunchKernelGGL(k_exact_explicit_bf16, dim3(a.n_items), dim3(64), 0, s, a);
+    if (bf16) hipLaunchKernelGGL(k_exact_explicit_bf16, dim3(a.n_items), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_exact_explicit_f32, dim3(a.n_items), dim3(64), 0, s, a);
   }
   return hipGetLastError();

@@ -144,24 +144,6 @@ constexpr int kK1XBytes = kRowsK1 * kK1Cols * 2;     // X1 bytes per stage (16 K
 constexpr int kK1XDma = kK1XBytes / 1024 / 4;        // 1 KB X1 instructions per wave per stage
 constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
 
-// s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt at max).
-#define DPN_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
-
-// 16 bytes per lane from global memory to LDS at lds_addr + 16 * lane
-// (lds_addr wave-uniform). M0 carries the LDS address; nothing else in these
-// kernels uses M0.
-__device__ __forceinline__ void dma16_stream(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-// Work-group barrier that the compiler may not move memory accesses across.
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int NCB, int HL>
 __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
@@ -387,13 +369,6 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
 constexpr int kK2Rows = 32;                              // rows of X2 per stage (one MFMA K step)
 constexpr int kK2XBytes = kK2Rows * kColsK2Bf16 * 2;     // X2 bytes per stage (32 KB)
 
-// s_waitcnt vmcnt(after * P) for after in 0..2.
-template <int P>
-__device__ __forceinline__ void wait_after(int after) {
-  if (after >= 2) DPN_WAIT_VMCNT(2 * P);
-  else if (after == 1) DPN_WAIT_VMCNT(P);
-  else DPN_WAIT_VMCNT(0);
-}
 
 template <int NCB, bool DIRECT>
 __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
