@@ -12,7 +12,7 @@
 // columns), by Cholesky QR in fp64, in three kernels:
 //   k_hpp_gram  : partial X^T X and X^T P over chunks of rows with fp64 MFMA
 //                 (v_mfma_f64_16x16x4), many work groups per sample;
-//   k_hpp_chol  : one wave per sample sums the partials in a fixed order and
+//   k_hpp_chol  : one work group per sample sums the partials in a fixed order and
 //                 factors X^T X = R^T R column by column in LDS (lane l fills
 //                 column l of each row of R) with a rank rule: column j is kept when its residual after
 //                 projecting out the kept columns before it (the Cholesky
@@ -100,10 +100,12 @@ __global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, i
   }
 }
 
-// One wave per sample: sum of the partial tiles, Cholesky with the rank rule,
-// Ri, M and N. Ri [B][MP][MP] and N [B][MP][32] go to global memory.
+// One work group per sample: sum of the partial tiles (all 256 threads, so
+// every lane's loads are in flight at once), Cholesky with the rank rule and
+// Ri (the first MP lanes, column by column), M and N (all threads).
+// Ri [B][MP][MP] and N [B][MP][32] go to global memory.
 template <int MP>
-__global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part, int nparts, float tau, double* Ri_g,
+__global__ void __launch_bounds__(256) k_hpp_chol(const double* __restrict__ part, int nparts, float tau, double* Ri_g,
                                                  double* N_g, int32_t* rank_out) {
   using H = HppTiles<MP>;
   constexpr int TA = H::TA, NG = H::NG, NT = H::NT;
@@ -111,7 +113,7 @@ __global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part
   const int i = blockIdx.x, l = threadIdx.x;
   const double* pi = part + (int64_t)i * nparts * NT * 256;
   // fixed-order sum; lane q, element j of a v_mfma_f64_16x16x4 result is (row q/16 + 4 j, column q % 16)
-  for (int e = l; e < NT * 256; e += 64) {
+  for (int e = l; e < NT * 256; e += 256) {
     double v = 0.0;
     for (int s0 = 0; s0 < nparts; s0 += 8) {  // eight loads in flight, summed in part order
       double w[8];
@@ -141,7 +143,7 @@ __global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part
 
   // Cholesky, column by column: every lane forms the residual of column j
   // (uniform LDS reads), then lane l > j fills R[j][l].
-  for (int e = l; e < MP * MP; e += 64) {
+  for (int e = l; e < MP * MP; e += 256) {
     (&R[0][0])[e] = 0.0;
     (&Ri[0][0])[e] = 0.0;
   }
@@ -181,9 +183,9 @@ __global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part
   }
   __syncthreads();
   double* Rig = Ri_g + (int64_t)i * MP * MP;
-  for (int e = l; e < MP * MP; e += 64) Rig[e] = (&Ri[0][0])[e];
+  for (int e = l; e < MP * MP; e += 256) Rig[e] = (&Ri[0][0])[e];
   // M[c][t] = sum_a Ri[a][c] XP[a][t]
-  for (int e = l; e < MP * kMaxTail; e += 64) {
+  for (int e = l; e < MP * kMaxTail; e += 256) {
     const int c = e / kMaxTail, t = e % kMaxTail;
     double v = 0.0;
     for (int a = 0; a <= c; ++a) v += Ri[a][c] * XP[a][t];
@@ -192,7 +194,7 @@ __global__ void __launch_bounds__(64) k_hpp_chol(const double* __restrict__ part
   __syncthreads();
   // N[a][t] = sum_c Ri[a][c] M[c][t]
   double* Ng = N_g + (int64_t)i * MP * kMaxTail;
-  for (int e = l; e < MP * kMaxTail; e += 64) {
+  for (int e = l; e < MP * kMaxTail; e += 256) {
     const int a = e / kMaxTail, t = e % kMaxTail;
     double v = 0.0;
     for (int c = a; c < MP; ++c) v += Ri[a][c] * M[c][t];
@@ -273,7 +275,7 @@ static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, in
   hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_hpp_chol<MP>, dim3(B), dim3(64), 0, s, part, nparts, tau, Ri, N, rank);
+  hipLaunchKernelGGL(k_hpp_chol<MP>, dim3(B), dim3(256), 0, s, part, nparts, tau, Ri, N, rank);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_hpp_apply<MP>, dim3((p + kApplyRows - 1) / kApplyRows, B), dim3(256), 0, s, X, p, mt, P,
