@@ -223,7 +223,20 @@ struct LoadG16 {
   __device__ __forceinline__ uint4 operator()(const void* p) const { return ldg16(p); }
 };
 
+// Gram, bf16: the K dimension (d for A A^T, then p for G G^T) is streamed
+// in 64-column chunks: each chunk's rows of the pair's two 128-row blocks
+// (2 x 16 KB, one 128-byte line per row) go to a 4-slot LDS ring by direct
+// loads, three chunks in flight. The 16-byte units of a row are XOR-swizzled
+// by the row index so the operand reads spread over the LDS banks; operands
+// need no transpose (K runs along the rows). Rows past T load row T - 1 and
+// their Gram entries are left out of the sum; K columns past d (p) are
+// zeroed in the chunk that holds them.
 __global__ void __launch_bounds__(256) k_exact_gram_bf16(ExactArgs a) {
+  constexpr int kBlk = 128 * 128;                 // one block's chunk: 128 rows x 128 bytes
+  constexpr int kStage = 2 * kBlk;
+  constexpr int kBufs = 4;
+  constexpr int kP = 2 * (kBlk / 1024 / 4);       // loads per wave per chunk
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
   __shared__ double red[4];
   const int per_i = a.tu * (a.tu + 1) / 2;
   const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
@@ -231,8 +244,36 @@ __global__ void __launch_bounds__(256) k_exact_gram_bf16(ExactArgs a) {
   int bt, bs;
   tri_pair(j, bt, bs);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
-  const int trow0 = 128 * bt + 64 * (wv >> 1), srow0 = 128 * bs + 64 * (wv & 1);
-  const int T = a.T;
+  const int T = a.T, d = a.d, p = a.p;
+  const int nA = (d + 63) / 64, nst = nA + (p + 63) / 64;
+  const uint16_t* Ab = (const uint16_t*)a.A + (int64_t)i * T * d;
+  const uint16_t* Gb = (const uint16_t*)a.G + (int64_t)i * T * p;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+
+  // loads: instruction j of wave wv fills rows 8 (4 wv + j) + lane / 8 of a
+  // block, at unit position lane % 8, which holds column unit (lane % 8) ^ (row % 8)
+  const int urow0 = 32 * wv + (lane >> 3);
+  const int gunit = (lane & 7) ^ (urow0 & 7);     // row % 8 is the same for all j
+  auto dma = [&](int st) {
+    if (st >= nst) return;
+    const bool onA = st < nA;
+    const uint16_t* M = onA ? Ab : Gb;
+    const int w = onA ? d : p;
+    int col = (onA ? st : st - nA) * 64 + 8 * gunit;
+    col = col < w ? col : w - 8;
+    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      int rt = 128 * bt + urow0 + 8 * jj, rs = 128 * bs + urow0 + 8 * jj;
+      rt = rt < T ? rt : T - 1;
+      rs = rs < T ? rs : T - 1;
+      const uint32_t off = (uint32_t)((wv * 4 + jj) * 1024);
+      dma16_stream(M + (int64_t)rt * w + col, buf + off);
+      dma16_stream(M + (int64_t)rs * w + col, buf + kBlk + off);
+    }
+  };
+
+  const int wy = wv >> 1, wx = wv & 1;
   f32x4_t ka[4][4], kg[4][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -241,15 +282,49 @@ __global__ void __launch_bounds__(256) k_exact_gram_bf16(ExactArgs a) {
       ka[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       kg[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  gram_tile_bf16<LoadG16>((const uint16_t*)a.A + (int64_t)i * T * a.d, T, a.d, trow0, srow0, ka, n, g);
-  gram_tile_bf16<LoadG16>((const uint16_t*)a.G + (int64_t)i * T * a.p, T, a.p, trow0, srow0, kg, n, g);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  // one chunk: two K steps of 32 over this wave's 64 x 64 quarter
+  auto chunk = [&](int st, int w, int c0, f32x4_t (&acc)[4][4]) {
+    const unsigned char* buf = lds + (st % kBufs) * kStage;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bool cok = c0 + 32 * kk + 8 * g < w;
+      uint4 ta[4], sb[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int rt = 64 * wy + 16 * m + n, rs = 64 * wx + 16 * m + n;
+        const uint4 xt = *(const uint4*)(buf + rt * 128 + (((4 * kk + g) ^ (rt & 7)) * 16));
+        const uint4 xs = *(const uint4*)(buf + kBlk + rs * 128 + (((4 * kk + g) ^ (rs & 7)) * 16));
+        ta[m] = cok ? xt : z;
+        sb[m] = xs;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[m][q] = mfma_bf16(ta[m], sb[q], acc[m][q]);
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < kBufs - 1; ++st) dma(st);
+  for (int st = 0; st < nst; ++st) {
+    wait_after<kP>(min(kBufs - 2, nst - 1 - st));
+    block_barrier();
+    dma(st + kBufs - 1);
+    if (st < nA) chunk(st, d, 64 * st, ka);
+    else chunk(st, p, 64 * (st - nA), kg);
+  }
+  // ka[m][q] lane (n, g), register r: Gram entry (t, s) with t = 128 bt + 64 wy
+  // + 16 m + 4 g + r and s = 128 bs + 64 wx + 16 q + n
   double ss = 0.0;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ss += (double)ka[m][q][r] * (double)kg[m][q][r];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 128 * bt + 64 * wy + 16 * m + 4 * g + r, u = 128 * bs + 64 * wx + 16 * q + n;
+        if (t < T && u < T) ss += (double)ka[m][q][r] * (double)kg[m][q][r];
+      }
   ss = wave_sum(ss);
   if (lane == 0) red[wv] = ss;
   __syncthreads();
