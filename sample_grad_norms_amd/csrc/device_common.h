@@ -155,4 +155,17 @@ __device__ __forceinline__ void wait_after(int after) {
   else DPN_WAIT_VMCNT(0);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 4 j + q supplies the address of 4 consecutive 16-bit elements; lane i
+// of the group receives element i % 4 of the data of lane 4 j + i / 4, for
+// j = 0..3. Pointing lane 4 j + q at row k0 + j, columns m0 + 4 q .. + 3 of a
+// row-major bf16 block gives lane i rows k0 .. k0 + 3 of column m0 + i: half
+// of a 16 x 32 MFMA operand (K along rows) with no register transpose.
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4_t*)
+                                                                 (__attribute__((address_space(3))) void*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 }  // namespace dpn

@@ -34,18 +34,32 @@ struct ExactArgs {
 // Every 32-row chunk of the tile's A and G columns (2 x 16 KB) is streamed
 // into LDS with direct global-to-LDS loads (four-slot ring, three chunks in
 // flight), so each A and G fragment is read from memory once for two waves.
-// A lane then reads 8 rows of its 8 consecutive columns of each operand from
-// LDS, transposes both 8 x 8 blocks so T runs along the MFMA K slots, and
-// issues the 64 MFMAs of its quarter. Rows past T and columns past d or p
-// load the last valid row / column and are zeroed after the LDS read.
-// Tiles are numbered with the A tile fastest, so the tiles one XCD takes (a
-// contiguous range) cover all of A for a few G tiles, and G is fetched from
-// HBM about once.
+// The MFMA operands (16 columns x 32 rows, T along K) are read straight from
+// the row-major chunk with transposing LDS reads; the 16-byte units of a row
+// are XOR-swizzled by the row index so the four rows of one such read fall on
+// different banks. Rows past T are loaded from a zero row; columns past d or
+// p load the last valid column and the W entries they make are left out of
+// the sum. Tiles are numbered with the A tile fastest, so the tiles one XCD
+// takes (a contiguous range) cover all of A for a few G tiles, and G is
+// fetched from HBM about once.
 // ---------------------------------------------------------------------------
 constexpr int kXTile = 256;                       // tile edge along d and along p
 constexpr int kXRows = 32;                        // rows per chunk (one MFMA K step)
 constexpr int kXOpBytes = kXRows * kXTile * 2;    // one operand's chunk (16 KB)
 constexpr int kXBufs = 4;                         // LDS ring: three chunks in flight, one in use
+
+__device__ __attribute__((aligned(16))) uint4 g_zero_row[kXTile / 8];  // 512 zero bytes (static storage)
+
+// 16 x 32 operand of columns m0 .. m0 + 15 from a swizzled 32 x 256 chunk:
+// K slot (g, s) is row slot_row(g, s), as in the other contractions.
+__device__ __forceinline__ uint4 tr_operand(const unsigned char* chunk, int m0, int n, int g) {
+  const int j = n >> 2, q = n & 3;
+  const int u = (m0 >> 3) + (q >> 1), half = (q & 1) * 8;
+  const int k1 = 4 * g + j, k2 = 16 + 4 * g + j;  // rows of K slots s = j and s = 4 + j
+  const uint2 lo = lds_read_tr16(chunk + k1 * 512 + ((u ^ (k1 & 7)) << 4) + half);
+  const uint2 hi = lds_read_tr16(chunk + k2 * 512 + ((u ^ (k2 & 7)) << 4) + half);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
 
 __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
   constexpr int kStage = 2 * kXOpBytes;           // A chunk, then G chunk
@@ -62,32 +76,34 @@ __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
   const int T = a.T, d = a.d, p = a.p;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
-  // loads: instruction j of wave wv fills chunk rows 8 wv + 2 j + lane / 32,
-  // 16-byte unit lane % 32 of the tile's 256 columns (512 bytes per row).
-  // Rows past T load row T - 1 (zeroed after the LDS read); columns past d
-  // or p load the last valid column, and the W entries they make are left
-  // out of the sum below.
-  const int drow = 8 * wv + (lane >> 5);
-  const int acol = min(kXTile * tu + 8 * (lane & 31), d - 8);
-  const int gcol = min(kXTile * tv + 8 * (lane & 31), p - 8);
-  const uint16_t* As = (const uint16_t*)a.A + (int64_t)i * T * d + acol;
-  const uint16_t* Gs = (const uint16_t*)a.G + (int64_t)i * T * p + gcol;
+  // loads: instruction j of wave wv fills chunk row 8 wv + 2 j + lane / 32 at
+  // unit position lane % 32, which holds the tile's column unit
+  // (lane % 32) ^ (row % 8) (512 bytes per row)
+  const int pos = lane & 31;
+  const uint16_t* Ab = (const uint16_t*)a.A + (int64_t)i * T * d;
+  const uint16_t* Gb = (const uint16_t*)a.G + (int64_t)i * T * p;
+  const unsigned char* zero = (const unsigned char*)g_zero_row + pos * 16;
+  int acol[kDma], gcol[kDma];
+#pragma unroll
+  for (int j = 0; j < kDma; ++j) {
+    const int unit = pos ^ ((2 * j + (lane >> 5)) & 7);
+    acol[j] = min(kXTile * tu + 8 * unit, d - 8);
+    gcol[j] = min(kXTile * tv + 8 * unit, p - 8);
+  }
   const int nch = (T + kXRows - 1) / kXRows;
   auto dma = [&](int c) {
     if (c >= nch) return;
     const uint32_t buf = lds_base + (uint32_t)((c % kXBufs) * kStage);
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-      int t = kXRows * c + drow + 2 * j;
-      t = t < T ? t : T - 1;
+      const int t = kXRows * c + 8 * wv + 2 * j + (lane >> 5);
       const uint32_t off = (uint32_t)((4 * wv + j) * 1024);
-      dma16_stream(As + (int64_t)t * d, buf + off);
-      dma16_stream(Gs + (int64_t)t * p, buf + kXOpBytes + off);
+      dma16_stream(t < T ? (const void*)(Ab + (int64_t)t * d + acol[j]) : (const void*)zero, buf + off);
+      dma16_stream(t < T ? (const void*)(Gb + (int64_t)t * p + gcol[j]) : (const void*)zero, buf + kXOpBytes + off);
     }
   };
 
   const int wa = wv & 1, wg = wv >> 1;
-  const int ao = (128 * wa + 8 * n) * 2, go = (128 * wg + 8 * n) * 2;  // byte offsets of this lane's columns
   f32x4_t acc[8][8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -101,25 +117,19 @@ __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
     block_barrier();
     dma(c + kXBufs - 1);
     const unsigned char* buf = lds + (c % kXBufs) * kStage;
-    const int t0 = kXRows * c;
-    uint4 ra[8], rg[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int r = slot_row(g, s);
-      const uint4 xa = *(const uint4*)(buf + r * 512 + ao);
-      ra[s] = t0 + r < T ? xa : make_uint4(0, 0, 0, 0);  // A rows past T are zero
-      rg[s] = *(const uint4*)(buf + kXOpBytes + r * 512 + go);
-    }
     uint4 oa[8], og[8];
-    transpose8x8_bf16(ra, oa);
-    transpose8x8_bf16(rg, og);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      oa[e] = tr_operand(buf, 128 * wa + 16 * e, n, g);
+      og[e] = tr_operand(buf + kXOpBytes, 128 * wg + 16 * e, n, g);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int f = 0; f < 8; ++f) acc[e][f] = mfma_bf16(oa[e], og[f], acc[e][f]);
   }
-  // acc[e][f] lane (n, g), register r: W[u][v] with u = column 128 wa + 8 (4 g + r) + e
-  // of the tile's A columns and v = 128 wg + 8 n + f of its G columns
+  // acc[e][f] lane (n, g), register r: W[u][v] with u = column 128 wa + 16 e + 4 g + r
+  // of the tile's A columns and v = 128 wg + 16 f + n of its G columns
   const int u0 = kXTile * tu + 128 * wa, v0 = kXTile * tv + 128 * wg;
   double ss = 0.0;
 #pragma unroll
@@ -129,7 +139,7 @@ __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const double y = (double)acc[e][f][r];
-        if (u0 + 8 * (4 * g + r) + e < d && v0 + 8 * n + f < p) ss += y * y;
+        if (u0 + 16 * e + 4 * g + r < d && v0 + 16 * f + n < p) ss += y * y;
       }
   ss = wave_sum(ss);
   if (lane == 0) red[wv] = ss;
