@@ -42,6 +42,10 @@ struct ExactArgs {
 // the sum. Tiles are numbered with the A tile fastest, so the tiles one XCD
 // takes (a contiguous range) cover all of A for a few G tiles, and G is
 // fetched from HBM about once.
+// With one wave per SIMD nothing hides a stall but the wave's own MFMAs, so
+// each chunk's 64 MFMAs run in shells of growing max(e, f): the first needs
+// two operands, not nine, and the eight loads of chunk c + 3 are spread over
+// the shells instead of issued as one block ahead of them.
 // ---------------------------------------------------------------------------
 constexpr int kXTile = 256;                       // tile edge along d and along p
 constexpr int kXRows = 32;                        // rows per chunk (one MFMA K step)
@@ -91,16 +95,14 @@ __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
     gcol[j] = min(kXTile * tv + 8 * unit, p - 8);
   }
   const int nch = (T + kXRows - 1) / kXRows;
-  auto dma = [&](int c) {
-    if (c >= nch) return;
-    const uint32_t buf = lds_base + (uint32_t)((c % kXBufs) * kStage);
-#pragma unroll
-    for (int j = 0; j < kDma; ++j) {
-      const int t = kXRows * c + 8 * wv + 2 * j + (lane >> 5);
-      const uint32_t off = (uint32_t)((4 * wv + j) * 1024);
-      dma16_stream(t < T ? (const void*)(Ab + (int64_t)t * d + acol[j]) : (const void*)zero, buf + off);
-      dma16_stream(t < T ? (const void*)(Gb + (int64_t)t * p + gcol[j]) : (const void*)zero, buf + kXOpBytes + off);
-    }
+  // Load j (0..3) of one operand of chunk c; chunks past the end load the
+  // zero row into a slot no later chunk uses, so every chunk issues the same
+  // loads and the waits below are constant.
+  auto dma = [&](int c, int j, int side) {
+    const int t = kXRows * c + 8 * wv + 2 * j + (lane >> 5);
+    const uint32_t buf = lds_base + (uint32_t)((c % kXBufs) * kStage + side * kXOpBytes + (4 * wv + j) * 1024);
+    const void* src = side ? (const void*)(Gb + (int64_t)t * p + gcol[j]) : (const void*)(Ab + (int64_t)t * d + acol[j]);
+    dma16(t < T ? src : (const void*)zero, buf);   // cached: four to eight work groups read each fragment
   };
 
   const int wa = wv & 1, wg = wv >> 1;
@@ -110,24 +112,37 @@ __global__ void __launch_bounds__(256) k_exact_explicit_bf16(ExactArgs a) {
 #pragma unroll
     for (int f = 0; f < 8; ++f) acc[e][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Each chunk's MFMAs run in shells s = max(e, f) = 0..7, so the first needs
+  // two operands; the operands of shell s + 1 and one load of chunk c + 3 are
+  // issued before shell s's MFMAs.
 #pragma unroll
-  for (int c = 0; c < kXBufs - 1; ++c) dma(c);
+  for (int c = 0; c < kXBufs - 1; ++c)
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) { dma(c, j, 0); dma(c, j, 1); }
   for (int c = 0; c < nch; ++c) {
-    wait_after<kP>(min(kXBufs - 2, nch - 1 - c));
+    DPN_WAIT_VMCNT(2 * kP);   // chunk c landed (chunks c + 1 and c + 2 may be in flight)
     block_barrier();
-    dma(c + kXBufs - 1);
     const unsigned char* buf = lds + (c % kXBufs) * kStage;
     uint4 oa[8], og[8];
+    oa[0] = tr_operand(buf, 128 * wa, n, g);
+    og[0] = tr_operand(buf + kXOpBytes, 128 * wg, n, g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      oa[e] = tr_operand(buf, 128 * wa + 16 * e, n, g);
-      og[e] = tr_operand(buf + kXOpBytes, 128 * wg + 16 * e, n, g);
+    for (int s = 0; s < 8; ++s) {
+      if (s < 7) {
+        oa[s + 1] = tr_operand(buf, 128 * wa + 16 * (s + 1), n, g);
+        og[s + 1] = tr_operand(buf + kXOpBytes, 128 * wg + 16 * (s + 1), n, g);
+      }
+      dma(c + kXBufs - 1, s >> 1, s & 1);
+#pragma unroll
+      for (int t = 0; t < s; ++t) {
+        acc[s][t] = mfma_bf16(oa[s], og[t], acc[s][t]);
+        acc[t][s] = mfma_bf16(oa[t], og[s], acc[t][s]);
+      }
+      acc[s][s] = mfma_bf16(oa[s], og[s], acc[s][s]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the shells in order (hoisting all reads costs registers)
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int f = 0; f < 8; ++f) acc[e][f] = mfma_bf16(oa[e], og[f], acc[e][f]);
   }
+  DPN_WAIT_VMCNT(0);   // the trailing zero-row loads land before the work group ends
   // acc[e][f] lane (n, g), register r: W[u][v] with u = column 128 wa + 16 e + 4 g + r
   // of the tile's A columns and v = 128 wg + 16 f + n of its G columns
   const int u0 = kXTile * tu + 128 * wa, v0 = kXTile * tv + 128 * wg;
