@@ -13,12 +13,12 @@
 //   k_hpp_gram  : partial X^T X and X^T P over chunks of rows with fp64 MFMA
 //                 (v_mfma_f64_16x16x4), many work groups per sample;
 //   k_hpp_chol  : one work group per sample sums the partials in a fixed order and
-//                 factors X^T X = R^T R column by column in LDS (lane l fills
-//                 column l of each row of R) with a rank rule: column j is kept when its residual after
+//                 factors X^T X = R^T R in LDS (right-looking, one entry of the
+//                 Schur complement per thread) with a rank rule: column j is kept when its residual after
 //                 projecting out the kept columns before it (the Cholesky
 //                 diagonal) exceeds tau times the largest column norm of X;
-//                 then Ri = R^-1 on the kept columns (zero rows and columns
-//                 elsewhere), M = Q^T P = Ri^T X^T P and N = Ri M;
+//                 the same eliminations on the identity give Ri = R^-1 on the kept columns (zero rows and columns
+//                 elsewhere); then M = Q^T P = Ri^T X^T P and N = Ri M;
 //   k_hpp_apply : Q = X Ri and P' = P - Q M = P - X N with fp64 MFMA.
 // Columns keep their positions: a dropped column of X gives a zero column of
 // Q, which adds nothing to the head. W3 = [Q (MP columns) | P' (m_t)].
@@ -141,46 +141,54 @@ __global__ void __launch_bounds__(256) k_hpp_chol(const double* __restrict__ par
   }
   __syncthreads();
 
-  // Cholesky, column by column: every lane forms the residual of column j
-  // (uniform LDS reads), then lane l > j fills R[j][l].
+  // Right-looking Cholesky on the Schur complement Sc (= G at the start), one
+  // entry per thread: at step j, if column j is kept, row j of R is row j of
+  // Sc over its diagonal root and every later entry (a, b) loses
+  // R[j][a] R[j][b]; so the diagonal Sc[j][j] a step reads is G[j][j] minus
+  // the squares of the kept rows above it, subtracted in row order. The same
+  // row operations on the identity give E = R^-T (rows of dropped columns
+  // are zeroed), so Ri = E^T needs no back substitution.
+  double (&Sc)[MP][MP] = G;
+  double (&E)[MP][MP] = Ri;
   for (int e = l; e < MP * MP; e += 256) {
     (&R[0][0])[e] = 0.0;
-    (&Ri[0][0])[e] = 0.0;
+    (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
   }
   double dmax = 0.0;
-  for (int j = 0; j < MP; ++j) dmax = fmax(dmax, G[j][j]);
+  for (int j = 0; j < MP; ++j) dmax = fmax(dmax, Sc[j][j]);
   const double scale = sqrt(fmax(dmax, 0.0));
   __syncthreads();
   uint32_t keep = 0;
   for (int j = 0; j < MP; ++j) {
-    double sj = G[j][j];
-    for (int c = 0; c < j; ++c)
-      if ((keep >> c) & 1u) sj -= R[c][j] * R[c][j];
-    const double nj = sqrt(fmax(sj, 0.0));
-    if (nj > (double)tau * scale && nj > 0.0) {
-      keep |= 1u << j;
-      if (l == j) R[j][j] = nj;
-      if (l > j && l < MP) {
-        double t = G[j][l];
-        for (int c = 0; c < j; ++c)
-          if ((keep >> c) & 1u) t -= R[c][j] * R[c][l];
-        R[j][l] = t / nj;
+    const double nj = sqrt(fmax(Sc[j][j], 0.0));
+    const bool kept = nj > (double)tau * scale && nj > 0.0;   // uniform
+    if (kept) keep |= 1u << j;
+    // row j of R and of E
+    for (int c = l; c < MP; c += 256) {
+      if (kept) {
+        R[j][c] = c == j ? nj : (c > j ? Sc[j][c] / nj : 0.0);
+        E[j][c] = E[j][c] / nj;
+      } else {
+        E[j][c] = 0.0;
+      }
+    }
+    __syncthreads();
+    if (kept) {
+      for (int e = l; e < MP * MP; e += 256) {
+        const int a = e / MP, b = e % MP;
+        if (a > j) {
+          const double ra = R[j][a];
+          if (b > j) Sc[a][b] -= ra * R[j][b];
+          E[a][b] -= ra * E[j][b];
+        }
       }
     }
     __syncthreads();
   }
-  // Ri: lane c computes column c by back substitution (zero off the kept columns)
-  if (l < MP && ((keep >> l) & 1u)) {
-    const int c = l;
-    Ri[c][c] = 1.0 / R[c][c];
-    for (int r = c - 1; r >= 0; --r) {
-      if (!((keep >> r) & 1u)) continue;
-      double t = 0.0;
-      for (int q = r + 1; q <= c; ++q)
-        if ((keep >> q) & 1u) t += R[r][q] * Ri[q][c];
-      Ri[r][c] = -t / R[r][r];
-    }
-  }
+  // Ri = E^T, back into Ri's storage (E aliases it): transpose via R, free now
+  for (int e = l; e < MP * MP; e += 256) (&R[0][0])[e] = E[e % MP][e / MP];
+  __syncthreads();
+  for (int e = l; e < MP * MP; e += 256) (&Ri[0][0])[e] = (&R[0][0])[e];
   __syncthreads();
   double* Rig = Ri_g + (int64_t)i * MP * MP;
   for (int e = l; e < MP * MP; e += 256) Rig[e] = (&Ri[0][0])[e];
