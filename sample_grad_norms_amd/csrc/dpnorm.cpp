@@ -598,8 +598,10 @@ dpnorm_status exact_plan(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64
   if (st != DPNORM_OK) return st;
   gram = route == DPNORM_EXACT_GRAM || (route == DPNORM_EXACT_AUTO && (double)d * (double)p > (double)T * (double)T);
   int32_t tu = 0, tv = 0;
-  const int64_t e = dt == DPNORM_BF16 ? 128 : 64;
-  const int64_t tiles = gram ? ((T + 127) / 128) * ((T + 127) / 128 + 1) / 2 : ((d + e - 1) / e) * ((p + e - 1) / e);
+  // work groups per sample, as exact_tiles counts them (in 64 bits first)
+  const bool bf16 = dt == DPNORM_BF16;
+  const int64_t e = bf16 ? 256 : 64, nt = (T + 255) / 256, mt = (T + 127) / 128;
+  const int64_t tiles = gram ? (bf16 ? nt * (nt + 1) : mt * (mt + 1) / 2) : ((d + e - 1) / e) * ((p + e - 1) / e);
   if (tiles * B >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;
   exact_tiles(dt == DPNORM_BF16, gram, T, d, p, tu, tv, slots);
   bytes = align_up(sizeof(double2) * (size_t)B * slots);

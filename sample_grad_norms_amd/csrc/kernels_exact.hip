@@ -8,9 +8,10 @@
 // accumulators (contraction over T, both operands transposed in registers)
 // and squared in place; nothing of size d x p is stored.
 // Gram route: n_i = <A_i A_i^T, G_i G_i^T>_F; a work group forms matching
-// 128 x 128 tiles of both Gram matrices (contractions over d and p, operands
-// read row-major as stored) and sums their elementwise product; tiles below
-// the diagonal count twice by symmetry and nothing of size T x T is stored.
+// tiles of both Gram matrices (contractions over d and p, operands read
+// row-major as stored; 256 x 128 in bf16, 128 x 128 in fp32) and sums their
+// elementwise product, each unordered pair of rows once with weight 2 off
+// the diagonal; nothing of size T x T is stored.
 // Both write one fp64 partial per tile; the per-sample finisher adds them in
 // a fixed order.
 #include "device_common.h"
@@ -218,145 +219,123 @@ __device__ __forceinline__ void tri_pair(int j, int& bt, int& bs) {
 }
 
 // ---------------------------------------------------------------------------
-// Gram, bf16: work group = 4 waves on a 128 (t) x 128 (s) tile pair, wave
-// (wy, wx) on 64 x 64. K steps of 32 over d (then p) read both operands
-// straight from the row-major rows of A (of G).
+// Gram, bf16: a work group takes rows t in [256 tb, 256 tb + 256) against
+// rows s in [128 sb, 128 sb + 128) of one sample, for every s block that
+// starts before the t block ends; entries weigh 2 (s < t), 1 (s = t) or 0
+// (s > t), so every unordered pair of rows counts once. Wave (wy, wx) holds
+// the 128 (t) x 64 (s) quarter of both Gram tiles, A A^T (K = d) then G G^T
+// (K = p), in 2 x 128 accumulator registers: 12 operand reads per 32 MFMAs.
+// K is streamed 32 columns at a time; a chunk is the pair's 384 rows x 64
+// bytes (24 KB), stored as 24 one-kilobyte pieces of 16 rows in MFMA operand
+// order (lane l holds row l % 16, columns 8 (l / 16) .. + 7), so an operand
+// is one contiguous, conflict-free 16-byte read per lane. A six-slot ring
+// keeps four chunks in flight; rows past T and columns past d (p) come from
+// a zero row, and chunks past the end load zero rows into a slot no later
+// chunk reads, so the waits are constant.
 // ---------------------------------------------------------------------------
-template <typename LoadOp>
-__device__ __forceinline__ void gram_tile_bf16(const uint16_t* M, int T, int w, int trow0, int srow0,
-                                               f32x4_t (&acc)[4][4], int n, int g) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  const int nks = (w + 31) >> 5;
-  for (int ks = 0; ks < nks; ++ks) {
-    const int col = 32 * ks + 8 * g;
-    const bool cok = col < w;
-    uint4 ta[4], sb[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int tr = trow0 + 16 * m + n, sr = srow0 + 16 * m + n;
-      ta[m] = (cok && tr < T) ? LoadOp()(M + (int64_t)tr * w + col) : z;
-      sb[m] = (cok && sr < T) ? LoadOp()(M + (int64_t)sr * w + col) : z;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[m][q] = mfma_bf16(ta[m], sb[q], acc[m][q]);
-  }
+constexpr int kGT = 256, kGS = 128;            // t and s rows of a tile pair
+constexpr int kGPieces = (kGT + kGS) / 16;     // 1 KB pieces per chunk (24)
+constexpr int kGChunk = kGPieces * 1024;       // 24 KB
+constexpr int kGBufs = 6;                      // 144 KB ring
+constexpr int kGLoads = kGPieces / 4;          // loads per wave per chunk (6)
+
+__device__ __forceinline__ void gram_pair(int j, int& tb, int& sb) {
+  int t = (int)((sqrt(4.0 * j + 1.0) - 1.0) * 0.5);  // t (t + 1) <= j < (t + 1) (t + 2)
+  while ((t + 1) * (t + 2) <= j) ++t;
+  while (t * (t + 1) > j) --t;
+  tb = t;
+  sb = j - t * (t + 1);
 }
 
-struct LoadG16 {
-  __device__ __forceinline__ uint4 operator()(const void* p) const { return ldg16(p); }
-};
-
-// Gram, bf16: the K dimension (d for A A^T, then p for G G^T) is streamed
-// in 64-column chunks: each chunk's rows of the pair's two 128-row blocks
-// (2 x 16 KB, one 128-byte line per row) go to a 4-slot LDS ring by direct
-// loads, three chunks in flight. The 16-byte units of a row are XOR-swizzled
-// by the row index so the operand reads spread over the LDS banks; operands
-// need no transpose (K runs along the rows). Rows past T load row T - 1 and
-// their Gram entries are left out of the sum; K columns past d (p) are
-// zeroed in the chunk that holds them.
 __global__ void __launch_bounds__(256) k_exact_gram_bf16(ExactArgs a) {
-  constexpr int kBlk = 128 * 128;                 // one block's chunk: 128 rows x 128 bytes
-  constexpr int kStage = 2 * kBlk;
-  constexpr int kBufs = 4;
-  constexpr int kP = 2 * (kBlk / 1024 / 4);       // loads per wave per chunk
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kGBufs * kGChunk];
   __shared__ double red[4];
-  const int per_i = a.tu * (a.tu + 1) / 2;
   const int item = xcd_item(blockIdx.x, (uint32_t)a.n_items);
-  const int i = item / per_i, j = item - i * per_i;
-  int bt, bs;
-  tri_pair(j, bt, bs);
+  const int i = item / a.slots, j = item - i * a.slots;
+  int tb, sb;
+  gram_pair(j, tb, sb);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
   const int T = a.T, d = a.d, p = a.p;
-  const int nA = (d + 63) / 64, nst = nA + (p + 63) / 64;
+  const int nA = (d + 31) / 32, nst = nA + (p + 31) / 32;
   const uint16_t* Ab = (const uint16_t*)a.A + (int64_t)i * T * d;
   const uint16_t* Gb = (const uint16_t*)a.G + (int64_t)i * T * p;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  const unsigned char* zero = (const unsigned char*)g_zero_row + (lane & 31) * 16;
 
-  // loads: instruction j of wave wv fills rows 8 (4 wv + j) + lane / 8 of a
-  // block, at unit position lane % 8, which holds column unit (lane % 8) ^ (row % 8)
-  const int urow0 = 32 * wv + (lane >> 3);
-  const int gunit = (lane & 7) ^ (urow0 & 7);     // row % 8 is the same for all j
+  int row[kGLoads];
+#pragma unroll
+  for (int jj = 0; jj < kGLoads; ++jj) {
+    const int pc = kGLoads * wv + jj;
+    const int r = pc < kGT / 16 ? kGT * tb + 16 * pc + n : kGS * sb + 16 * (pc - kGT / 16) + n;
+    row[jj] = r < T ? r : -1;
+  }
   auto dma = [&](int st) {
-    if (st >= nst) return;
     const bool onA = st < nA;
     const uint16_t* M = onA ? Ab : Gb;
     const int w = onA ? d : p;
-    int col = (onA ? st : st - nA) * 64 + 8 * gunit;
-    col = col < w ? col : w - 8;
-    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage);
+    const int col = (onA ? st : st - nA) * 32 + 8 * g;
+    const uint32_t buf = lds_base + (uint32_t)((st % kGBufs) * kGChunk);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      int rt = 128 * bt + urow0 + 8 * jj, rs = 128 * bs + urow0 + 8 * jj;
-      rt = rt < T ? rt : T - 1;
-      rs = rs < T ? rs : T - 1;
-      const uint32_t off = (uint32_t)((wv * 4 + jj) * 1024);
-      dma16_stream(M + (int64_t)rt * w + col, buf + off);
-      dma16_stream(M + (int64_t)rs * w + col, buf + kBlk + off);
+    for (int jj = 0; jj < kGLoads; ++jj) {
+      const bool ok = st < nst && row[jj] >= 0 && col < w;
+      dma16(ok ? (const void*)(M + (int64_t)row[jj] * w + col) : (const void*)zero,
+            buf + (uint32_t)((kGLoads * wv + jj) * 1024));
     }
   };
-
   const int wy = wv >> 1, wx = wv & 1;
-  f32x4_t ka[4][4], kg[4][4];
+  f32x4_t ka[8][4], kg[8][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       ka[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       kg[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  // one chunk: two K steps of 32 over this wave's 64 x 64 quarter
-  auto chunk = [&](int st, int w, int c0, f32x4_t (&acc)[4][4]) {
-    const unsigned char* buf = lds + (st % kBufs) * kStage;
+  auto chunk = [&](int st, f32x4_t (&acc)[8][4]) {
+    const unsigned char* buf = lds + (st % kGBufs) * kGChunk + lane * 16;
+    uint4 sv[4], tv[8];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bool cok = c0 + 32 * kk + 8 * g < w;
-      uint4 ta[4], sb[4];
+    for (int q = 0; q < 4; ++q) sv[q] = *(const uint4*)(buf + (kGT / 16 + 4 * wx + q) * 1024);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int rt = 64 * wy + 16 * m + n, rs = 64 * wx + 16 * m + n;
-        const uint4 xt = *(const uint4*)(buf + rt * 128 + (((4 * kk + g) ^ (rt & 7)) * 16));
-        const uint4 xs = *(const uint4*)(buf + kBlk + rs * 128 + (((4 * kk + g) ^ (rs & 7)) * 16));
-        ta[m] = cok ? xt : z;
-        sb[m] = xs;
-      }
+    for (int m = 0; m < 8; ++m) tv[m] = *(const uint4*)(buf + (8 * wy + m) * 1024);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[m][q] = mfma_bf16(ta[m], sb[q], acc[m][q]);
-    }
+      for (int q = 0; q < 4; ++q) acc[m][q] = mfma_bf16(tv[m], sv[q], acc[m][q]);
   };
 #pragma unroll
-  for (int st = 0; st < kBufs - 1; ++st) dma(st);
-  for (int st = 0; st < nst; ++st) {
-    wait_after<kP>(min(kBufs - 2, nst - 1 - st));
+  for (int st = 0; st < kGBufs - 1; ++st) dma(st);
+  for (int st = 0; st < nA; ++st) {
+    DPN_WAIT_VMCNT((kGBufs - 2) * kGLoads);
     block_barrier();
-    dma(st + kBufs - 1);
-    if (st < nA) chunk(st, d, 64 * st, ka);
-    else chunk(st, p, 64 * (st - nA), kg);
+    dma(st + kGBufs - 1);
+    chunk(st, ka);
   }
-  // ka[m][q] lane (n, g), register r: Gram entry (t, s) with t = 128 bt + 64 wy
-  // + 16 m + 4 g + r and s = 128 bs + 64 wx + 16 q + n
+  for (int st = nA; st < nst; ++st) {
+    DPN_WAIT_VMCNT((kGBufs - 2) * kGLoads);
+    block_barrier();
+    dma(st + kGBufs - 1);
+    chunk(st, kg);
+  }
+  DPN_WAIT_VMCNT(0);   // the trailing zero-row loads land before the work group ends
+  // acc[m][q] lane (n, g), register r: Gram entry (t, s) with t = 256 tb +
+  // 128 wy + 16 m + 4 g + r and s = 128 sb + 64 wx + 16 q + n
   double ss = 0.0;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 128 * bt + 64 * wy + 16 * m + 4 * g + r, u = 128 * bs + 64 * wx + 16 * q + n;
-        if (t < T && u < T) ss += (double)ka[m][q][r] * (double)kg[m][q][r];
+        const int t = kGT * tb + 128 * wy + 16 * m + 4 * g + r, u = kGS * sb + 64 * wx + 16 * q + n;
+        const double wgt = (t >= T || u > t) ? 0.0 : (u < t ? 2.0 : 1.0);
+        ss += wgt * ((double)ka[m][q][r] * (double)kg[m][q][r]);
       }
   ss = wave_sum(ss);
   if (lane == 0) red[wv] = ss;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const double wgt = bs < bt ? 2.0 : 1.0;
-    a.partials[(int64_t)i * a.slots + j] = make_double2(wgt * ((red[0] + red[1]) + (red[2] + red[3])), 0.0);
-  }
+  if (threadIdx.x == 0)
+    a.partials[(int64_t)i * a.slots + j] = make_double2((red[0] + red[1]) + (red[2] + red[3]), 0.0);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,10 +404,16 @@ __global__ void __launch_bounds__(256) k_exact_gram_f32(ExactArgs a) {
   }
 }
 
-// Work decomposition shared with the host: explicit tiles are 128 x 128
-// (bf16) or 64 x 64 (fp32) of W_i; Gram tiles are 128 x 128 pairs (t >= s).
+// Work decomposition shared with the host: explicit tiles are 256 x 256
+// (bf16) or 64 x 64 (fp32) of W_i; Gram work groups take 256 (t) x 128 (s)
+// pairs, nT (nT + 1) of them for nT = ceil(T / 256) (bf16), or 128 x 128
+// pairs with t >= s (fp32).
 void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots) {
-  if (gram) {
+  if (gram && bf16) {
+    tu = (int32_t)((T + kGT - 1) / kGT);
+    tv = tu;
+    slots = tu * (tu + 1);
+  } else if (gram) {
     tu = (int32_t)((T + 127) / 128);
     tv = tu;
     slots = tu * (tu + 1) / 2;

@@ -10,7 +10,8 @@
 
 The summary is a markdown file holding the commands, the tables and one
 JSON block; ``read_traffic`` returns the traffic of a kernel from that block
-when the block's source hash still matches the kernel sources, else None.
+when the block's hash of the sources it names (the csrc files the profiled
+kernels are built from) still matches them, else None.
 
 Usage: python -m sample_grad_norms_amd.profiling --trace DIR --fetch DIR
 --write DIR --out FILE --cmd "..." [--cmd "..."]
@@ -31,14 +32,20 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 CALIB_BYTES = 1 << 30
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and headers of the library."""
+def source_files() -> List[str]:
+    """Names of the library's HIP sources and headers (csrc/)."""
+    return sorted(os.path.basename(p) for p in glob.glob(os.path.join(HERE, "csrc", "*"))
+                  if p.endswith((".hip", ".h", ".cpp")))
+
+
+def source_hash(files: Optional[List[str]] = None) -> str:
+    """sha256 over the named csrc files (default: all of them). A file that
+    no longer exists hashes as missing, so the summary reads as stale."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        if path.endswith((".hip", ".h", ".cpp")):
-            with open(path, "rb") as f:
-                h.update(os.path.basename(path).encode())
-                h.update(f.read())
+    for name in sorted(files if files is not None else source_files()):
+        h.update(name.encode())
+        path = os.path.join(HERE, "csrc", name)
+        h.update(open(path, "rb").read() if os.path.exists(path) else b"<missing>")
     return h.hexdigest()
 
 
@@ -86,12 +93,14 @@ def scaled_bytes(vals: Dict[str, List[float]]) -> Dict[str, float]:
     return {k: sum(v) / len(v) * 1024.0 * factor for k, v in vals.items()}, factor
 
 
-def summarize(trace_dir: str, fetch_dir: str, write_dir: str, out: str, cmds: List[str], title: str) -> Dict:
+def summarize(trace_dir: str, fetch_dir: str, write_dir: str, out: str, cmds: List[str], title: str,
+              sources: Optional[List[str]] = None) -> Dict:
     stats = kernel_stats(trace_dir)
     fetch, ffac = scaled_bytes(counter_values(fetch_dir, "FETCH_SIZE"))
     write, wfac = scaled_bytes(counter_values(write_dir, "WRITE_SIZE"))
     traffic = {k: fetch.get(k, 0.0) + write.get(k, 0.0) for k in set(fetch) | set(write) if k.startswith("k_")}
-    block = {"source_sha256": source_hash(), "fetch_scale": ffac, "write_scale": wfac,
+    files = sorted(sources) if sources else source_files()
+    block = {"source_files": files, "source_sha256": source_hash(files), "fetch_scale": ffac, "write_scale": wfac,
              "traffic_bytes_per_dispatch": traffic,
              "fetch_bytes_per_dispatch": {k: v for k, v in fetch.items() if k.startswith("k_")},
              "write_bytes_per_dispatch": {k: v for k, v in write.items() if k.startswith("k_")},
@@ -124,7 +133,7 @@ def read_traffic(path: str, kernel_prefix: str) -> Optional[float]:
     ``kernel_prefix``, or None when the summary is missing or the kernel
     sources changed since it was taken."""
     block = read_block(path)
-    if not block or block.get("source_sha256") != source_hash():
+    if not block or block.get("source_sha256") != source_hash(block.get("source_files")):
         return None
     for k, v in block["traffic_bytes_per_dispatch"].items():
         if k.startswith(kernel_prefix):
@@ -140,8 +149,11 @@ def main() -> None:
     ap.add_argument("--out", required=True)
     ap.add_argument("--title", default="rocprofv3 summary")
     ap.add_argument("--cmd", action="append", default=[])
+    ap.add_argument("--sources", nargs="*", default=None,
+                    help="csrc files the profiled kernels are built from (default: all); the summary "
+                         "reads as stale once any of them changes")
     a = ap.parse_args()
-    block = summarize(a.trace, a.fetch, a.write, a.out, a.cmd, a.title)
+    block = summarize(a.trace, a.fetch, a.write, a.out, a.cmd, a.title, a.sources)
     print(json.dumps(block["traffic_bytes_per_dispatch"]))
 
 

@@ -38,7 +38,8 @@ def test_config1_fp32_exact():
 
 
 @pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 1e-3), (torch.float32, 1e-5)])
-@pytest.mark.parametrize("B,T,d,p", [(2, 333, 264, 136), (1, 1, 8, 8), (3, 260, 1032, 520), (2, 40, 200, 72)])
+@pytest.mark.parametrize("B,T,d,p", [(2, 333, 264, 136), (1, 1, 8, 8), (3, 260, 1032, 520), (2, 40, 200, 72),
+                                     (1, 777, 96, 40)])
 @pytest.mark.parametrize("route", ["explicit", "gram"])
 def test_exact_shapes(dtype, tol, B, T, d, p, route):
     import sample_grad_norms_amd as dp
