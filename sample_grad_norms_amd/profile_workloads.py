@@ -8,6 +8,7 @@ NAME is one of:
   long_context_exact  the exact explicit route on the same inputs
   hutchpp             Hutch++, B=4, T=4096, d=p=2048, budget 32
   single_layer        Hutchinson, B=8, T=1024, d=p=2048, k=32
+  single_layer_gram   the exact Gram route on the same inputs
 --calib-copy first runs one 1 GiB device-to-device copy, the reference the
 counter summaries scale FETCH_SIZE and WRITE_SIZE by.
 """
@@ -21,7 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-NAMES = ("long_context_hutch", "long_context_exact", "hutchpp", "single_layer")
+NAMES = ("long_context_hutch", "long_context_exact", "hutchpp", "single_layer", "single_layer_gram")
 
 
 def main() -> None:
@@ -47,7 +48,7 @@ def main() -> None:
         fn = lambda: dp.hutchpp(pr.A, pr.G, pr.S, pr.P, k=pr.k)
     else:
         pr = workloads.config2(device=dev)
-        fn = lambda: dp.hutch(pr.A, pr.G, pr.P)
+        fn = (lambda: dp.exact(pr.A, pr.G, route="gram")) if a.name.endswith("gram") else (lambda: dp.hutch(pr.A, pr.G, pr.P))
     for _ in range(a.reps):
         fn()
     torch.cuda.synchronize()
