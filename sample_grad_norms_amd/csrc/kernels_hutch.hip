@@ -46,8 +46,14 @@ __device__ __forceinline__ float w_value(const PrepLayer& P, int smp, int v, int
 
 __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
   const int first = blockIdx.x * 256;
-  int l = 0;
-  while (l + 1 < a.nlayers && first >= a.L[l + 1].unit_begin) ++l;
+  // the last layer whose first unit is <= first (binary search over the
+  // kernel-argument table: a few dependent scalar loads, not one per layer)
+  int l = 0, hi = a.nlayers - 1;
+  while (l < hi) {
+    const int mid = (l + hi + 1) >> 1;
+    if (a.L[mid].unit_begin <= first) l = mid;
+    else hi = mid - 1;
+  }
   const PrepLayer& P = a.L[l];
   int r = first + threadIdx.x - P.unit_begin;
   if (r >= P.n_pack + P.n1 + P.n2 + 1) return;  // padding up to the next layer's first work group
