@@ -26,6 +26,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetItems = 1024;   // stage-2 work items wanted before T is split
 constexpr int kMinChunksPerSplit = 16;   // >= 512 rows per T split
+constexpr int64_t kMinItems = 256;       // below this many items (one per CU), splits may be shorter
+constexpr int kMinChunksPerSplitSmall = 8;  // ... down to 256 rows
 constexpr int kMaxK = 64;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -150,11 +152,19 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
     g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
     base_items += pl.B * g.ubs;
   }
+  // Split T when there are few (layer, sample, column block) items: more
+  // splits fill the CUs but write and re-read more partial tiles, so splits
+  // keep at least 512 rows, or 256 while the launch would leave CUs idle.
   pl.nsplit = 1;
   if (base_items < kTargetItems) {
     const int max_split = std::max(1, pl.nch / kMinChunksPerSplit);
     const int64_t want = (kTargetItems + base_items - 1) / base_items;
     pl.nsplit = (int)std::min<int64_t>(want, max_split);
+    if (base_items * pl.nsplit < kMinItems) {
+      const int max_small = std::max(1, pl.nch / kMinChunksPerSplitSmall);
+      const int64_t fill = (kMinItems + base_items - 1) / base_items;
+      pl.nsplit = std::max(pl.nsplit, (int)std::min<int64_t>(fill, max_small));
+    }
   }
   // stage-1 items, largest rows first so the launch ends on short items
   std::vector<int> order(nl);
