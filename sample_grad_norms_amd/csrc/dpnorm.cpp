@@ -74,6 +74,7 @@ struct PassPlan {
   int NCB = 2, HL = 1;
   int64_t B = 0, T = 0, Tpad = 0;
   int nch = 0, nsplit = 1, cols2 = kColsK2Bf16, rbs = 0;
+  int rows1 = kRowsK1;  // rows per stage-1 item
   bool store = false;
   bool fuse = false;            // group layers that share X2
   size_t off_recs = 0, off_items1 = 0, off_items2 = 0, off_partials = 0;
@@ -136,7 +137,9 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   const int nl = (int)L.size();
   pl.Tpad = (pl.T + kRowsK1 - 1) / kRowsK1 * kRowsK1;
   pl.nch = (int)((pl.T + 31) / 32);
-  pl.rbs = (int)(pl.Tpad / kRowsK1);
+  // bf16 stage 1 takes 64-row items when 128-row items would leave CUs idle
+  pl.rows1 = pl.bf16 && (int64_t)nl * pl.B * (pl.Tpad / kRowsK1) < kMinItems ? kRowsK1Small : kRowsK1;
+  pl.rbs = (int)(pl.Tpad / pl.rows1);
   pl.cols2 = pl.bf16 ? kColsK2Bf16 : kColsK2F32;
   form_groups(pl, L);
   const int ng = (int)pl.groups.size();
@@ -336,7 +339,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
 
   st.items = items1;
   st.n_items = (int32_t)pl.total1;
-  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, s));
+  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, s));
   DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
 
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {
@@ -453,7 +456,7 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
       pl.ld = sign ? (k + 31) / 32 : k;
       pl.ncols = (int)k;
     }
-    items1 += B * ((T + kRowsK1 - 1) / kRowsK1);
+    items1 += B * ((T + kRowsK1Small - 1) / kRowsK1Small);
     items2 += B * ((pl.w2 + kColsK2F32 - 1) / kColsK2F32) * 64;
   }
   if (items1 >= ((int64_t)1 << 31) || items2 >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;

@@ -16,6 +16,7 @@
 namespace dpn {
 
 constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
+constexpr int kRowsK1Small = 64;  // same with 2 waves (bf16, when 128-row items leave CUs idle)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 256;   // elements of a Y tile per split-T reduction work group (one wave)
@@ -70,7 +71,7 @@ struct PrepArgs {
   int32_t nlayers, total_units;
   int32_t NCB, HL;         // packed W: column blocks of 16, hi/lo halves (bf16 target)
   int32_t f32_target;      // pack W as fp32 rows [rows16][NC] instead of bf16 fragments
-  int32_t rbs;             // stage-1 row blocks per sample (Tpad / kRowsK1)
+  int32_t rbs;             // stage-1 row blocks per sample (Tpad / rows per item)
   int32_t nsplit;          // stage-2 T splits
 };
 
@@ -87,7 +88,7 @@ struct StageArgs {
 enum Mode : int32_t { MODE_SQ = 0, MODE_STORE = 1 };
 
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStream_t s);
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, hipStream_t s);
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).

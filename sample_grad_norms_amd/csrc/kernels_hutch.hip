@@ -146,16 +146,18 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
 // V layout: [B][Tpad/32][NCB][2][64] uint4.
 // ---------------------------------------------------------------------------
 constexpr int kK1Cols = 64;                          // columns of X1 per stage (one 128-byte line)
-constexpr int kK1XBytes = kRowsK1 * kK1Cols * 2;     // X1 bytes per stage (16 KB)
-constexpr int kK1XDma = kK1XBytes / 1024 / 4;        // 1 KB X1 instructions per wave per stage
+constexpr int kK1XDma = 32 * kK1Cols * 2 / 1024;     // 1 KB X1 instructions per wave per stage (its 32 rows)
 constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
 
-
-template <int NCB, int HL>
-__global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
+// NW waves, 32 NW rows per item: 4 (128 rows) normally, 2 (64 rows) when
+// 128-row items would leave CUs idle.
+template <int NCB, int HL, int NW>
+__global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
+  constexpr int kRows = 32 * NW;
+  constexpr int kK1XBytes = kRows * kK1Cols * 2;         // X1 bytes per stage (16 KB for 4 waves)
   constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per stage
   constexpr int kStage = kK1XBytes + kWBlocks * 1024;
-  constexpr int kPerWave = kK1XDma + kWBlocks / 4;       // loads every wave issues per stage (at least)
+  constexpr int kPerWave = kK1XDma + kWBlocks / NW;      // loads every wave issues per stage (at least)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kK1Bufs * kStage];
   const int4 it = a.items[blockIdx.x];
   const LayerRec* L = a.recs + it.x;
@@ -163,7 +165,7 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int w = L->w1, T = a.T;
-  const int r0 = rb * kRowsK1;
+  const int r0 = rb * kRows;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
   const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
   const int nst = (w + kK1Cols - 1) / kK1Cols;
@@ -190,8 +192,8 @@ __global__ void __launch_bounds__(256) k_rowproj_bf16(StageArgs a) {
       dma16_stream(X + (int64_t)row * w + col, buf + (uint32_t)((wv * kK1XDma + j) * 1024));
     }
 #pragma unroll
-    for (int m0 = 0; m0 < (kWBlocks + 3) / 4; ++m0) {
-      const int m = 4 * m0 + wv;
+    for (int m0 = 0; m0 < (kWBlocks + NW - 1) / NW; ++m0) {
+      const int m = NW * m0 + wv;
       if (m < kWBlocks) dma16(Wp + ((int64_t)cst * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
     }
   };
@@ -613,20 +615,29 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, hipStream_t s) {
+template <int NW>
+static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, hipStream_t s) {
+  const dim3 grid(a.n_items), blk(64 * NW);
+  if (HL == 1) {
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW>), grid, blk, 0, s, a);
+  } else {
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2, NW>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2, NW>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_bf16<4, 2, NW>), grid, blk, 0, s, a);
+  }
+}
+
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid(a.n_items), blk(256);
   if (bf16) {
-    if (HL == 1) {
-      if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1>), grid, blk, 0, s, a);
-      else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_rowproj_bf16<4, 1>), grid, blk, 0, s, a);
-    } else {
-      if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2>), grid, blk, 0, s, a);
-      else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_rowproj_bf16<4, 2>), grid, blk, 0, s, a);
-    }
+    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, s);
+    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, s);
+    else return hipErrorInvalidValue;
   } else {
+    if (rows1 != kRowsK1) return hipErrorInvalidValue;
     if (NCB == 1) hipLaunchKernelGGL((k_rowproj_f32<1>), grid, blk, 0, s, a);
     else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_f32<2>), grid, blk, 0, s, a);
     else hipLaunchKernelGGL((k_rowproj_f32<4>), grid, blk, 0, s, a);
