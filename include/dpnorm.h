@@ -234,7 +234,8 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
  * note 研究背景与动机 and 相关工作, explicit gradients vs ghost clipping;
  * summary: Complexiteitsreductie). DPNORM_EXACT_EXPLICIT sums squares of
  * A^T G tiles (2 T d p flops per sample); DPNORM_EXACT_GRAM sums the product
- * of A A^T and G G^T tiles (about 2 T^2 (d + p) flops with symmetry); AUTO
+ * of A A^T and G G^T tiles (about T^2 (d + p) flops per sample using their
+ * symmetry, 2 T^2 (d + p) without); AUTO
  * picks explicit when d*p <= T*T. Nothing of size d x p or T x T is stored.
  * The workspace holds one fp64 partial per tile and sample. */
 dpnorm_status dpnorm_exact(const void* A, const void* G, dpnorm_dtype dt, int64_t B, int64_t T, int64_t d,
