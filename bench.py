@@ -69,10 +69,12 @@ def cpu_baseline(layers, B, T, n_layers):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    spent = 0.0
+    spent = copy_s = 0.0
     parts = []
     for (A, G, P) in layers[: 7 * n_layers]:
+        t0 = time.perf_counter()
         a, g, p = oracle.to_f64(A), oracle.to_f64(G), oracle.to_f64(P)
+        copy_s += time.perf_counter() - t0
         t0 = time.perf_counter()
         parts.append(oracle.hutch(a, g, p))
         spent += time.perf_counter() - t0
@@ -84,7 +86,23 @@ def cpu_baseline(layers, B, T, n_layers):
     return {"value": B * T / step_s, "unit": "samples·tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 numpy oracle over {n_layers} decoder layer(s) x 7 projections, all {B} samples, "
                       f"T={T}: {spent:.2f} s of oracle arithmetic"
-                      + ("" if n_layers == 16 else f", scaled x{16 / n_layers:g} to the step")}
+                      + ("" if n_layers == 16 else f", scaled x{16 / n_layers:g} to the step")
+                      + f" (device-to-host copies and fp64 conversion, untimed in the rate: {copy_s:.2f} s)",
+            "host": host_cpu()}
+
+
+def host_cpu() -> str:
+    """The host's CPU model and logical CPU count (from /proc/cpuinfo)."""
+    model, n = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    n += 1
+                    model = line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return f"{model}, {n or os.cpu_count()} logical CPUs"
 
 
 def rotated(make, copies):
