@@ -382,7 +382,7 @@ def extras(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (the per-sample norm path needs no collectives); "
+        print("bench.py measures a single GPU (the per-sample norm path needs no exchange between GPUs); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
