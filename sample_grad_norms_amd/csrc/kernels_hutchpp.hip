@@ -9,17 +9,19 @@
 // on the complement, ||A^T G (I - Q Q^T) P||_F^2.
 //
 // Q is the Q factor of X with positive diagonal (unique for the kept
-// columns), by Cholesky QR in fp64, in three kernels:
+// columns), by Cholesky QR in fp64, in two kernels:
 //   k_hpp_gram  : partial X^T X and X^T P over chunks of rows with fp64 MFMA
 //                 (v_mfma_f64_16x16x4), many work groups per sample;
-//   k_hpp_chol  : one work group per sample sums the partials in a fixed order and
-//                 factors X^T X = R^T R in LDS (right-looking, one entry of the
-//                 Schur complement per thread) with a rank rule: column j is kept when its residual after
-//                 projecting out the kept columns before it (the Cholesky
-//                 diagonal) exceeds tau times the largest column norm of X;
-//                 the same eliminations on the identity give Ri = R^-1 on the kept columns (zero rows and columns
-//                 elsewhere); then M = Q^T P = Ri^T X^T P and N = Ri M;
-//   k_hpp_apply : Q = X Ri and P' = P - Q M = P - X N with fp64 MFMA.
+//   k_hpp_apply : every work group first sums its sample's partials in a
+//                 fixed order and factors X^T X = R^T R in LDS (right-looking,
+//                 one entry of the Schur complement per thread) with a rank
+//                 rule: column j is kept when its residual after projecting
+//                 out the kept columns before it (the Cholesky diagonal)
+//                 exceeds tau times the largest column norm of X; the same
+//                 eliminations on the identity give Ri = R^-1 on the kept
+//                 columns (zero rows and columns elsewhere); M = Q^T P =
+//                 Ri^T X^T P and N = Ri M; then
+//                 Q = X Ri and P' = P - Q M = P - X N with fp64 MFMA.
 // Columns keep their positions: a dropped column of X gives a zero column of
 // Q, which adds nothing to the head. W3 = [Q (MP columns) | P' (m_t)].
 // The rank rule bounds the condition number of the kept columns by about
@@ -100,17 +102,27 @@ __global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, i
   }
 }
 
-// One work group per sample: sum of the partial tiles (all 256 threads, so
-// every lane's loads are in flight at once), Cholesky with the rank rule and
-// Ri (the first MP lanes, column by column), M and N (all threads).
-// Ri [B][MP][MP] and N [B][MP][32] go to global memory.
+// The basis of one sample in LDS: the Gram tiles summed from their partials,
+// R with the rank rule, Ri = R^-1 on the kept columns, M = Q^T P and N = Ri M.
 template <int MP>
-__global__ void __launch_bounds__(256) k_hpp_chol(const double* __restrict__ part, int nparts, float tau, double* Ri_g,
-                                                 double* N_g, int32_t* rank_out) {
+struct HppBasis {
+  double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail], N[MP][kMaxTail];
+};
+
+// Run by all 256 threads of a work group (it holds barriers): sum of sample
+// i's partial tiles in a fixed order (every lane's loads in flight at once),
+// Cholesky with the rank rule, Ri, M and N. Every work group that runs it on
+// the same partials gets bitwise the same basis. Returns the kept columns.
+template <int MP>
+__device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float tau, int i, HppBasis<MP>& sb) {
   using H = HppTiles<MP>;
   constexpr int TA = H::TA, NG = H::NG, NT = H::NT;
-  __shared__ double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail];
-  const int i = blockIdx.x, l = threadIdx.x;
+  double (&G)[MP][MP] = sb.G;
+  double (&XP)[MP][kMaxTail] = sb.XP;
+  double (&R)[MP][MP] = sb.R;
+  double (&Ri)[MP][MP] = sb.Ri;
+  double (&M)[MP][kMaxTail] = sb.M;
+  const int l = threadIdx.x;
   const double* pi = part + (int64_t)i * nparts * NT * 256;
   // fixed-order sum; lane q, element j of a v_mfma_f64_16x16x4 result is (row q/16 + 4 j, column q % 16)
   for (int e = l; e < NT * 256; e += 256) {
@@ -190,8 +202,6 @@ __global__ void __launch_bounds__(256) k_hpp_chol(const double* __restrict__ par
   __syncthreads();
   for (int e = l; e < MP * MP; e += 256) (&Ri[0][0])[e] = (&R[0][0])[e];
   __syncthreads();
-  double* Rig = Ri_g + (int64_t)i * MP * MP;
-  for (int e = l; e < MP * MP; e += 256) Rig[e] = (&Ri[0][0])[e];
   // M[c][t] = sum_a Ri[a][c] XP[a][t]
   for (int e = l; e < MP * kMaxTail; e += 256) {
     const int c = e / kMaxTail, t = e % kMaxTail;
@@ -201,30 +211,34 @@ __global__ void __launch_bounds__(256) k_hpp_chol(const double* __restrict__ par
   }
   __syncthreads();
   // N[a][t] = sum_c Ri[a][c] M[c][t]
-  double* Ng = N_g + (int64_t)i * MP * kMaxTail;
   for (int e = l; e < MP * kMaxTail; e += 256) {
     const int a = e / kMaxTail, t = e % kMaxTail;
     double v = 0.0;
     for (int c = a; c < MP; ++c) v += Ri[a][c] * M[c][t];
-    Ng[e] = v;
+    sb.N[a][t] = v;
   }
-  if (l == 0 && rank_out) rank_out[i] = __popc(keep);
+  __syncthreads();
+  return keep;
 }
 
 // Q = X Ri and P' = P - X N for kApplyRows rows (16 per wave); K slot l / 16
-// is column 4 ks + l / 16 of X.
+// is column 4 ks + l / 16 of X. Each work group first forms its sample's
+// basis from the Gram partials itself (a few microseconds of LDS work), which
+// costs less than a launch of its own between the two kernels.
 template <int MP>
 __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, int p, int mt,
                                                    const void* __restrict__ P, int ptype,
-                                                   const double* __restrict__ Ri_g, const double* __restrict__ N_g,
-                                                   float* W3, int ldw) {
+                                                   const double* __restrict__ part, int nparts, float tau,
+                                                   int32_t* rank_out, float* W3, int ldw) {
   constexpr int TA = MP / 16;
-  __shared__ double Ri[MP][MP], N[MP][kMaxTail];
+  __shared__ HppBasis<MP> sb;
   const int i = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  for (int e = tid; e < MP * MP; e += 256) (&Ri[0][0])[e] = Ri_g[(int64_t)i * MP * MP + e];
-  for (int e = tid; e < MP * kMaxTail; e += 256) (&N[0][0])[e] = N_g[(int64_t)i * MP * kMaxTail + e];
+  const uint32_t keep = hpp_basis<MP>(part, nparts, tau, i, sb);
+  if (blockIdx.x == 0 && tid == 0 && rank_out) rank_out[i] = __popc(keep);
+  double (&Ri)[MP][MP] = sb.Ri;
+  double (&N)[MP][kMaxTail] = sb.N;
   const float* Xi = X + (int64_t)i * p * MP;
   float* Wi = W3 + (int64_t)i * p * ldw;
   const int r0 = blockIdx.x * kApplyRows + 16 * wv;
@@ -268,26 +282,19 @@ size_t hpp_qr_scratch_bytes(int MP, int B, int p) {
   const int nparts = (p + kGramRows - 1) / kGramRows;
   const int NT = MP == 16 ? HppTiles<16>::NT : HppTiles<32>::NT;
   const size_t part = (size_t)B * nparts * NT * 256 * 8;
-  const size_t ri = (size_t)B * MP * MP * 8, nn = (size_t)B * MP * kMaxTail * 8;
-  return ((part + 255) / 256 + (ri + 255) / 256 + (nn + 255) / 256) * 256;
+  return (part + 255) / 256 * 256;
 }
 
 template <int MP>
 static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
                          int ldw, int32_t* rank, char* scratch, hipStream_t s) {
   const int nparts = (p + kGramRows - 1) / kGramRows;
-  constexpr int NT = HppTiles<MP>::NT;
   double* part = (double*)scratch;
-  double* Ri = (double*)(scratch + ((size_t)B * nparts * NT * 256 * 8 + 255) / 256 * 256);
-  double* N = (double*)((char*)Ri + ((size_t)B * MP * MP * 8 + 255) / 256 * 256);
   hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_hpp_chol<MP>, dim3(B), dim3(256), 0, s, part, nparts, tau, Ri, N, rank);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_hpp_apply<MP>, dim3((p + kApplyRows - 1) / kApplyRows, B), dim3(256), 0, s, X, p, mt, P,
-                     ptype, Ri, N, W3, ldw);
+                     ptype, (const double*)part, nparts, tau, rank, W3, ldw);
   return hipGetLastError();
 }
 
