@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, i
 template <int MP>
 struct HppBasis {
   double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail], N[MP][kMaxTail];
+  double sj[MP];   // 1 / R[j][j] of kept columns, 0 of dropped ones
 };
 
 // Run by all 256 threads of a work group (it holds barriers): sum of sample
@@ -154,18 +155,18 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   __syncthreads();
 
   // Right-looking Cholesky on the Schur complement Sc (= G at the start), one
-  // entry per thread: at step j, if column j is kept, row j of R is row j of
-  // Sc over its diagonal root and every later entry (a, b) loses
+  // entry per thread: at step j, if column j is kept, row j of R (formed only
+  // where needed) is row j of Sc times 1 / Sc[j][j]^(1/2) and every later entry (a, b) loses
   // R[j][a] R[j][b]; so the diagonal Sc[j][j] a step reads is G[j][j] minus
   // the squares of the kept rows above it, subtracted in row order. The same
-  // row operations on the identity give E = R^-T (rows of dropped columns
-  // are zeroed), so Ri = E^T needs no back substitution.
+  // row operations on the identity give E = R^-T: row j of E is scaled by the
+  // same factor, which is kept in sj[] and applied once at the end (rows of
+  // dropped columns get 0), so a step reads only row j, which it never writes,
+  // and needs one barrier.
   double (&Sc)[MP][MP] = G;
   double (&E)[MP][MP] = Ri;
-  for (int e = l; e < MP * MP; e += 256) {
-    (&R[0][0])[e] = 0.0;
-    (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
-  }
+  double (&sj)[MP] = sb.sj;
+  for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
   double dmax = 0.0;
   for (int j = 0; j < MP; ++j) dmax = fmax(dmax, Sc[j][j]);
   const double scale = sqrt(fmax(dmax, 0.0));
@@ -174,30 +175,24 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   for (int j = 0; j < MP; ++j) {
     const double nj = sqrt(fmax(Sc[j][j], 0.0));
     const bool kept = nj > (double)tau * scale && nj > 0.0;   // uniform
+    const double inv = kept ? 1.0 / nj : 0.0;
     if (kept) keep |= 1u << j;
-    // row j of R and of E
-    for (int c = l; c < MP; c += 256) {
-      if (kept) {
-        R[j][c] = c == j ? nj : (c > j ? Sc[j][c] / nj : 0.0);
-        E[j][c] = E[j][c] / nj;
-      } else {
-        E[j][c] = 0.0;
-      }
-    }
-    __syncthreads();
+    if (l == 0) sj[j] = inv;
     if (kept) {
       for (int e = l; e < MP * MP; e += 256) {
-        const int a = e / MP, b = e % MP;
-        if (a > j) {
-          const double ra = R[j][a];
-          if (b > j) Sc[a][b] -= ra * R[j][b];
-          E[a][b] -= ra * E[j][b];
+        const int r = e / MP, c = e % MP;
+        if (r > j) {
+          const double rr = Sc[j][r] * inv;                   // R[j][r]
+          if (c > j) Sc[r][c] -= rr * (Sc[j][c] * inv);
+          E[r][c] -= rr * (E[j][c] * inv);
         }
       }
     }
     __syncthreads();
   }
-  // Ri = E^T, back into Ri's storage (E aliases it): transpose via R, free now
+  for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] *= sj[e / MP];
+  __syncthreads();
+  // Ri = E^T, back into Ri's storage (E aliases it): transpose via R (scratch)
   for (int e = l; e < MP * MP; e += 256) (&R[0][0])[e] = E[e % MP][e / MP];
   __syncthreads();
   for (int e = l; e < MP * MP; e += 256) (&Ri[0][0])[e] = (&R[0][0])[e];
