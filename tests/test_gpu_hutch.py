@@ -59,6 +59,8 @@ SHAPES_BF16 = [
     (4, 200, 136, 64, 64),       # k = 64 (four column blocks)
     (2, 128, 2048, 512, 16),     # one 16-column block
     (1, 2500, 4096, 8192, 32),   # long rows on both sides, split T
+    (32, 1000, 264, 136, 32),    # 256 stage-1 items of 128 rows (four waves), ragged T and widths
+    (31, 1000, 264, 136, 32),    # 248 such items: 64-row two-wave items instead
 ]
 
 
