@@ -14,7 +14,9 @@ when the block's hash of the sources it names (the csrc files the profiled
 kernels are built from) still matches them, else None.
 
 Usage: python -m sample_grad_norms_amd.profiling --trace DIR --fetch DIR
---write DIR --out FILE --cmd "..." [--cmd "..."]
+--write DIR --out FILE --cmd "..." [--cmd "..."], or, for utilisation
+counters (MFMA, LDS, waits, L2 hits) of one or more --pmc runs,
+python -m sample_grad_norms_amd.profiling --pmc DIR [--pmc DIR] --out FILE
 """
 from __future__ import annotations
 
@@ -141,11 +143,81 @@ def read_traffic(path: str, kernel_prefix: str) -> Optional[float]:
     return None
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU. GRBM_GUI_ACTIVE is reported summed
+# over the XCDs, so one XCD's active cycles are the sum over N_XCD.
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+# (label, numerator, denominator, scale) of the derived utilisation figures
+DERIVED = (
+    ("MFMA pipe busy (per SIMD)", "SQ_VALU_MFMA_BUSY_CYCLES", "simd_cycles", 1.0),
+    ("LDS busy (indexed ops, per CU)", "SQ_LDS_IDX_ACTIVE", "cu_cycles", 1.0),
+    ("LDS cycles stalled by bank conflicts / LDS busy", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", 1.0),
+    ("wave time waiting on a dependency (s_waitcnt)", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", 1.0),
+    ("L2 hit rate", "TCC_HIT_sum", "tcc_requests", 1.0),
+)
+
+
+def counter_means(pmc_dirs: List[str]) -> Dict[str, Dict[str, float]]:
+    """Mean per dispatch of every counter of every dpn:: kernel, over the
+    counter_collection.csv files of several --pmc runs."""
+    out: Dict[str, Dict[str, List[float]]] = {}
+    for d in pmc_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no *counter_collection.csv under {d}")
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                if "dpn::" not in r["Kernel_Name"]:
+                    continue
+                out.setdefault(short_name(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in out.items()}
+
+
+def derived(c: Dict[str, float]) -> Dict[str, Optional[float]]:
+    """Utilisation ratios of one kernel's mean counters (None where a counter is missing)."""
+    v = dict(c)
+    if "GRBM_GUI_ACTIVE" in v:
+        cycles = v["GRBM_GUI_ACTIVE"] / N_XCD
+        v["simd_cycles"] = cycles * N_SIMD
+        v["cu_cycles"] = cycles * N_CU
+    if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v:
+        v["tcc_requests"] = v["TCC_HIT_sum"] + v["TCC_MISS_sum"]
+    res: Dict[str, Optional[float]] = {}
+    for label, num, den, scale in DERIVED:
+        res[label] = scale * v[num] / v[den] if num in v and v.get(den) else None
+    return res
+
+
+def counters_summary(pmc_dirs: List[str], out: str, cmds: List[str], title: str) -> Dict:
+    """Markdown summary of utilisation counters per kernel (means per dispatch
+    and the ratios of DERIVED)."""
+    means = counter_means(pmc_dirs)
+    names = sorted({c for cs in means.values() for c in cs})
+    lines = [f"# {title}", "", "Commands (run from the repository root on the GPU box):", "", "```", *cmds, "```", "",
+             "## Utilisation", "", "| kernel | " + " | ".join(l for (l, _, _, _) in DERIVED) + " |",
+             "|---" * (len(DERIVED) + 1) + "|"]
+    for k in sorted(means):
+        dv = derived(means[k])
+        lines.append(f"| {k} | " + " | ".join("—" if dv[l] is None else f"{100 * dv[l]:.1f} %"
+                                               for (l, _, _, _) in DERIVED) + " |")
+    lines += ["", f"Cycles: GRBM_GUI_ACTIVE / {N_XCD} (it is summed over the XCDs); {N_SIMD} SIMDs, {N_CU} CUs.", "",
+              "## Mean counter values per dispatch", "", "| kernel | " + " | ".join(names) + " |",
+              "|---" * (len(names) + 1) + "|"]
+    for k in sorted(means):
+        lines.append(f"| {k} | " + " | ".join(f"{means[k][c]:.4g}" if c in means[k] else "—" for c in names) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return means
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--pmc", action="append", default=[],
+                    help="utilisation mode: a --pmc run directory (repeat for several runs)")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--out", required=True)
     ap.add_argument("--title", default="rocprofv3 summary")
     ap.add_argument("--cmd", action="append", default=[])
@@ -153,6 +225,11 @@ def main() -> None:
                     help="csrc files the profiled kernels are built from (default: all); the summary "
                          "reads as stale once any of them changes")
     a = ap.parse_args()
+    if a.pmc:
+        counters_summary(a.pmc, a.out, a.cmd, a.title)
+        return
+    if not (a.trace and a.fetch and a.write):
+        ap.error("--trace, --fetch and --write are required (or --pmc for the utilisation summary)")
     block = summarize(a.trace, a.fetch, a.write, a.out, a.cmd, a.title, a.sources)
     print(json.dumps(block["traffic_bytes_per_dispatch"]))
 

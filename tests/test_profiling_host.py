@@ -76,3 +76,29 @@ def test_missing_calibration_copy_is_an_error(tmp_path):
     trace, fetch, write = fake_runs(tmp_path, 0.0, 0.0)
     with pytest.raises(ValueError):
         profiling.summarize(trace, fetch, write, str(tmp_path / "x.md"), [], "t")
+
+
+def test_utilisation_summary(tmp_path):
+    run = tmp_path / "pmc" / "box"
+    run.mkdir(parents=True)
+    rows = []
+    for v in (1.0, 3.0):   # two dispatches: means 2x the base values
+        rows += [["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "GRBM_GUI_ACTIVE", 8e6 * v],
+                 ["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "SQ_VALU_MFMA_BUSY_CYCLES", 0.25e6 * 1024 * v],
+                 ["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "SQ_LDS_IDX_ACTIVE", 0.5e6 * 256 * v],
+                 ["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "SQ_LDS_BANK_CONFLICT", 0.1e6 * 256 * v],
+                 ["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "TCC_HIT_sum", 3.0 * v],
+                 ["void dpn::k_rowproj_bf16<2, 1, 4>(dpn::StageArgs)", "TCC_MISS_sum", 1.0 * v],
+                 ["__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 5.0]]
+    write_csv(str(run / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    out = str(tmp_path / "u.md")
+    means = profiling.counters_summary([str(tmp_path / "pmc")], out, ["cmd"], "title")
+    assert list(means) == ["k_rowproj_bf16<2, 1, 4>"]          # library kernels only
+    d = profiling.derived(means["k_rowproj_bf16<2, 1, 4>"])
+    assert d["MFMA pipe busy (per SIMD)"] == pytest.approx(0.25)   # 2e6 cycles per XCD, a quarter busy
+    assert d["LDS busy (indexed ops, per CU)"] == pytest.approx(0.5)
+    assert d["LDS cycles stalled by bank conflicts / LDS busy"] == pytest.approx(0.2)
+    assert d["L2 hit rate"] == pytest.approx(0.75)
+    assert d["wave time waiting on a dependency (s_waitcnt)"] is None
+    text = open(out).read()
+    assert "25.0 %" in text and "75.0 %" in text
