@@ -75,3 +75,12 @@ def test_config5_full_size_explicit():
     n = dp.exact(prob.A, prob.G)  # d p <= T^2: the explicit route
     torch.cuda.synchronize()
     check(n.cpu(), oracle.exact_explicit(prob.A, prob.G), 1e-3, "config5 exact (explicit)")
+
+
+@pytest.mark.parametrize("route", ["explicit", "gram"])
+def test_exact_is_bitwise_deterministic(route):
+    import sample_grad_norms_amd as dp
+    pr = workloads.random_problem(3, 777, 264, 136, 8, seed=11, device=dev(), dtype=torch.bfloat16)
+    runs = [dp.exact(pr.A, pr.G, route=route).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(runs[0], r) for r in runs[1:])

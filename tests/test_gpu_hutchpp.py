@@ -92,3 +92,19 @@ def test_hutchpp_accumulates():
     torch.cuda.synchronize()
     want = oracle.hutchpp(pr.A, pr.G, S, P)[0] + 3.0
     assert np.all(rel(base.cpu(), want) <= 1e-3)
+
+
+def test_hutchpp_is_bitwise_deterministic():
+    """Every work group of the apply kernel forms its sample's basis itself;
+    they must agree, and repeated calls must give the same bits."""
+    import sample_grad_norms_amd as dp
+    B, T, d, p, k = 3, 600, 264, 520, 32
+    ms, mt = oracle.hutchpp_split(k)
+    pr = workloads.random_problem(B, T, d, p, k, seed=21, device=dev(), dtype=torch.bfloat16)
+    S = workloads.gaussian((p, ms), 1.0, 22, dev(), torch.bfloat16)
+    P = workloads.projection(p, mt, 23, dev(), torch.bfloat16)
+    runs = [tuple(t.clone() for t in dp.hutchpp(pr.A, pr.G, S, P, return_parts=True)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
