@@ -106,10 +106,30 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 in[8], uint4 out[8
 // the lane's own registers.
 __device__ __forceinline__ int slot_row(int g, int s) { return 16 * (s >> 2) + 4 * g + (s & 3); }
 
+// One DPP move of a double (both 32-bit halves); lanes whose source lies
+// outside their row, or whose row is masked off, receive 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint2 h = __builtin_bit_cast(uint2, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h.x, CTRL, ROW_MASK, 0xf, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h.y, CTRL, ROW_MASK, 0xf, true);
+  return __builtin_bit_cast(double, make_uint2(lo, hi));
+}
+
+// Sum over the 64 lanes, the same in every lane, in a fixed order: inclusive
+// prefix sums within each row of 16 lanes (DPP row_shr 1, 2, 4, 8), then
+// lane 15 of rows 0 and 2 added into rows 1 and 3 (row_bcast:15) and lane 31
+// into rows 2 and 3 (row_bcast:31), so lane 63 holds the total.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_f64<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);   // row_shr:8
+  v += dpp_f64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  const uint2 h = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(double, make_uint2((uint32_t)__builtin_amdgcn_readlane((int)h.x, 63),
+                                               (uint32_t)__builtin_amdgcn_readlane((int)h.y, 63)));
 }
 
 // Map a linear block index to a work item so that each XCD (blocks are
