@@ -353,7 +353,29 @@ def extras(args):
         "hutchpp_ms": ms, "hutchpp_samples_tokens_per_s": B * T / (ms * 1e-3),
         "hutchpp_hbm_gbs_3_streams": byt / ms / 1e6, "hutch_same_inputs_ms": msh,
         "hutchpp_over_hutch_time": ms / msh}
-    del sets, ws, wsh
+    # the ghost-clipping (Gram) route on the same T = 4096 inputs, beside Hutchinson
+    wsg = torch.empty(dp.exact_workspace(torch.bfloat16, B, T, d, p, "gram"), dtype=torch.uint8, device=dev)
+    msg = timed(lambda: dp.exact(sets[0].A, sets[0].G, route="gram", workspace=wsg), 10, 10)
+    gram_over_hutch = msg / msh
+    del sets, ws, wsh, wsg
+
+    # the pages' relative figures (context, on their hardware where they name one), beside ours
+    Bm, Tm, dm, pm, km = 4, 4096, 8192, 2048, 32   # the largest Llama-3.2-1B layer (down), T = 4096, k = 32
+    ws_big = dp.hutch_workspace(torch.bfloat16, Bm, Tm, dm, pm, km)
+    grads = Bm * dm * pm * 4                       # fp32 per-sample gradients, materialised
+    out["pages_figures_beside_ours"] = {
+        "hutch_vs_hutchpp_time": {"pages": "Hutch about 3x faster than Hutch++ (A100 80GB)",
+                                  "ours": ms / msh, "workload": "B=4, T=4096, d=p=2048, budget 32"},
+        "hutch_vs_ghost_clipping": {"pages": "128x fewer FLOPs at T=4096, k=32",
+                                    "flop_ratio_full_gram": Tm / km,            # 2 T^2 (d+p) against 2 T k (d+p)
+                                    "flop_ratio_gram_route_with_symmetry": Tm / (2 * km),
+                                    "measured_time_ratio": gram_over_hutch, "ghost_gram_ms": msg,
+                                    "workload": "B=4, T=4096, d=p=2048, the Gram route against Hutchinson"},
+        "hutch_vs_explicit_flop_saving_largest_layer": {"pages": "98.05 %",
+                                                        "closed_form": 1 - km * (dm + pm) / (dm * pm)},
+        "memory_saving_excl_inputs_largest_layer": {"pages": "99.22 %", "closed_form": 1 - Tm * km / (dm * pm),
+                                                    "ours_workspace_bytes": ws_big,
+                                                    "ours_vs_fp32_per_sample_gradients": 1 - ws_big / grads}}
 
     # long context, B=1 T=32768 d=2048 p=8192: Hutchinson and the exact (explicit) comparator side by side
     pr = workloads.config5(device=dev)
