@@ -254,14 +254,65 @@ struct Tracer {
     if (e_ != hipSuccess) return e_;               \
   } while (0)
 
-// The record of prepare-table entry e (pl.entries) is recs[e].
-hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, hipStream_t s,
-                    Tracer& tr) {
+// Prepare-table entry e of a pass (pl.entries): its record and what the
+// prepare kernel derives from it. The record of entry e is recs[e].
+void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, int e, PrepLayer& P) {
+  std::memset(&P, 0, sizeof(P));
+  LayerRec& R = P.rec;
+  R.split = 1 << 30;
+  const int le = pl.entries[e].first, ge = pl.entries[e].second;
+  if (le >= 0) {  // stage-1 projection
+    const PassLayer& in = L[le];
+    const PassGroup& g = pl.groups[pl.group_of[le]];
+    R.X1 = in.X1;
+    R.W = base + pl.off_W[le];
+    R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
+    R.w1 = (int32_t)in.w1;
+    if (pl.bf16) {
+      R.V = (uint4*)(base + g.off_V) + (size_t)pl.jb0[le] * 2 * 64;
+      R.vstride = g.ncb * 2 * 64;
+    } else {
+      R.V = (float*)(base + g.off_V) + (size_t)pl.jb0[le] * 16;
+      R.vstride = 16 * g.ncb;
+    }
+    P.wsrc = in.wsrc;
+    P.wsrc_stride_b = in.wsrc_stride_b;
+    P.wsrc_type = in.wsrc_type;
+    P.ld = (int32_t)in.ld;
+    P.ncols = in.ncols;
+    P.nsamples = in.nsamples;
+    P.n_pack = pl.n_pack[le];
+    P.k1_begin = pl.k1_begin[le];
+    P.n1 = pl.n1[le];
+  }
+  if (ge >= 0) {  // stage-2 group (V is the group's whole V, at offset 0 for a lone layer)
+    const PassGroup& g = pl.groups[ge];
+    const PassLayer& in = L[g.members[0]];
+    R.X2 = in.X2;
+    R.V = base + g.off_V;
+    R.vstride = pl.bf16 ? g.ncb * 2 * 64 : 16 * g.ncb;
+    R.Ypart = pl.nsplit > 1 ? (float*)(base + g.off_Yp) : (pl.store ? in.Yout : nullptr);
+    R.Yout = in.Yout;
+    R.w2 = (int32_t)in.w2;
+    R.slot_base = g.slot_base;
+    R.split = in.split;
+    P.k2_begin = g.k2_begin;
+    P.n2 = g.n2;
+    P.ubs = g.ubs;
+  }
+  P.layer = e;
+}
+
+// prepare = false: the tables and packed W are already in place (written by
+// the kernel that produced W); ysum = false: the split-T partial tiles are
+// left for the caller to reduce.
+hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, hipStream_t s, Tracer& tr,
+                    bool prepare = true, bool ysum = true) {
   const int entries = (int)pl.entries.size();
   LayerRec* recs = (LayerRec*)(base + pl.off_recs);
   int4* items1 = (int4*)(base + pl.off_items1);
   int4* items2 = (int4*)(base + pl.off_items2);
-  for (int c0 = 0; c0 < entries; c0 += kPrepChunk) {
+  for (int c0 = 0; prepare && c0 < entries; c0 += kPrepChunk) {
     PrepArgs a;
     std::memset(&a, 0, sizeof(a));
     a.recs = recs;
@@ -275,51 +326,8 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
     int units = 0;
     const int cn = std::min(kPrepChunk, entries - c0);
     for (int j = 0; j < cn; ++j) {
-      const int e = c0 + j;
       PrepLayer& P = a.L[j];
-      LayerRec& R = P.rec;
-      R.split = 1 << 30;
-      const int le = pl.entries[e].first, ge = pl.entries[e].second;
-      if (le >= 0) {  // stage-1 projection
-        const PassLayer& in = L[le];
-        const PassGroup& g = pl.groups[pl.group_of[le]];
-        R.X1 = in.X1;
-        R.W = base + pl.off_W[le];
-        R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
-        R.w1 = (int32_t)in.w1;
-        if (pl.bf16) {
-          R.V = (uint4*)(base + g.off_V) + (size_t)pl.jb0[le] * 2 * 64;
-          R.vstride = g.ncb * 2 * 64;
-        } else {
-          R.V = (float*)(base + g.off_V) + (size_t)pl.jb0[le] * 16;
-          R.vstride = 16 * g.ncb;
-        }
-        P.wsrc = in.wsrc;
-        P.wsrc_stride_b = in.wsrc_stride_b;
-        P.wsrc_type = in.wsrc_type;
-        P.ld = (int32_t)in.ld;
-        P.ncols = in.ncols;
-        P.nsamples = in.nsamples;
-        P.n_pack = pl.n_pack[le];
-        P.k1_begin = pl.k1_begin[le];
-        P.n1 = pl.n1[le];
-      }
-      if (ge >= 0) {  // stage-2 group (V is the group's whole V, at offset 0 for a lone layer)
-        const PassGroup& g = pl.groups[ge];
-        const PassLayer& in = L[g.members[0]];
-        R.X2 = in.X2;
-        R.V = base + g.off_V;
-        R.vstride = pl.bf16 ? g.ncb * 2 * 64 : 16 * g.ncb;
-        R.Ypart = pl.nsplit > 1 ? (float*)(base + g.off_Yp) : (pl.store ? in.Yout : nullptr);
-        R.Yout = in.Yout;
-        R.w2 = (int32_t)in.w2;
-        R.slot_base = g.slot_base;
-        R.split = in.split;
-        P.k2_begin = g.k2_begin;
-        P.n2 = g.n2;
-        P.ubs = g.ubs;
-      }
-      P.layer = e;
+      fill_entry(pl, L, base, c0 + j, P);
       P.unit_begin = units;
       units += (P.n_pack + P.n1 + P.n2 + 1 + 255) / 256 * 256;  // next entry starts a work group
     }
@@ -347,12 +355,38 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
     st.n_items = pl.class_end[c] - pl.class_begin[c];
     DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.direct(), s));
     DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
-    if (pl.needs_ysum()) {
+    if (pl.needs_ysum() && ysum) {
       DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, s));
       DPN_TRY(tr.mark(DPNORM_KERNEL_YSUM));
     }
   }
   return hipSuccess;
+}
+
+// The tables and packed W of a pass over one layer whose W is per-sample fp32
+// with bf16 hi/lo packing, for a kernel that writes them in place of that
+// pass's prepare launch; false when the pass is not of that form.
+bool next_tables(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, HppNext& nx) {
+  if (!pl.bf16 || pl.HL != 2 || L.size() != 1 || pl.entries.size() != 1 || L[0].wsrc_type != SRC_F32) return false;
+  PrepLayer P;
+  fill_entry(pl, L, base, 0, P);
+  if (P.k1_begin != 0 || P.k2_begin != 0 || P.rec.w_stride_b == 0) return false;
+  std::memset(&nx, 0, sizeof(nx));
+  nx.rec = P.rec;
+  nx.recs = (LayerRec*)(base + pl.off_recs);
+  nx.items1 = (int4*)(base + pl.off_items1);
+  nx.items2 = (int4*)(base + pl.off_items2);
+  nx.W = (uint4*)P.rec.W;
+  nx.w_stride_b = P.rec.w_stride_b;
+  nx.n1 = P.n1;
+  nx.rbs = pl.rbs;
+  nx.n2 = P.n2;
+  nx.ubs = P.ubs;
+  nx.nsplit = pl.nsplit;
+  nx.rows = (int32_t)L[0].w1;
+  nx.ncols = P.ncols;
+  nx.NCB = pl.NCB;
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -787,12 +821,22 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   float* W3 = (float*)(base + hc.off_w3);
   int32_t* rk = (int32_t*)(base + hc.off_rank);
   Tracer tr;
-  hipError_t he = run_pass(hc.p1, hc.l1, base, stream, tr);
-  if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr);
+  // In bf16, the kernels that produce pass 2's and pass 3's projections (the
+  // split-T sum of pass 1, the basis kernel) also pack them and write those
+  // passes' tables, so neither pass launches its prepare kernel.
+  HppNext nx2, nx3;
+  const bool fuse2 = hc.p1.needs_ysum() && hc.p1.groups.size() == 1 && next_tables(hc.p2, hc.l2, base, nx2);
+  const bool fuse3 = next_tables(hc.p3, hc.l3, base, nx3);
+  hipError_t he = run_pass(hc.p1, hc.l1, base, stream, tr, true, !fuse2);
+  if (he == hipSuccess && fuse2)
+    he = launch_hpp_ysum_pack((const float*)(base + hc.p1.groups[0].off_Yp), hc.p1.nsplit, (int)B, (int)d, hc.NC1,
+                              nx2, stream);
+  if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr, !fuse2);
   if (he == hipSuccess)
     he = launch_hpp_qr((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.mt, P,
-                       dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, base + hc.off_qr, stream);
-  if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr);
+                       dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, base + hc.off_qr,
+                       fuse3 ? &nx3 : nullptr, stream);
+  if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr, !fuse3);
   if (he == hipSuccess)
     he = launch_finish((const double2*)(base + hc.p3.off_partials), (int32_t)B, hc.p3.slots, n, accumulate, head,
                        tail, nullptr, 1.f, 0, 1.0, stream);

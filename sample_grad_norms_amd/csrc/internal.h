@@ -107,8 +107,33 @@ hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t
 // columns)], rank per sample into rank [B]. `scratch` holds
 // hpp_qr_scratch_bytes(MP, B, p) bytes (256-byte aligned).
 size_t hpp_qr_scratch_bytes(int MP, int B, int p);
+
+// The tables of a single-layer bf16 pass (record 0, both work lists) and its
+// packed projection, for a kernel that produces the projection to write in
+// place of that pass's prepare launch: W (the record's packed W) holds the
+// hi/lo bf16 fragments of an fp32 matrix with `rows` rows and `ncols` valid
+// columns, in NCB 16-column blocks, w_stride_b units per sample, as the
+// prepare kernel packs them.
+struct HppNext {
+  LayerRec rec;
+  LayerRec* recs;
+  int4* items1;
+  int4* items2;
+  uint4* W;
+  int64_t w_stride_b;
+  int32_t n1, rbs, n2, ubs, nsplit;
+  int32_t rows, ncols, NCB;
+};
+
+// next == nullptr: W3 is written; else next's packed W (from the same values) and
+// tables are written in its place, and W3 is not.
 hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, void* scratch, hipStream_t s);
+                         int ldw, int32_t* rank, void* scratch, const HppNext* next, hipStream_t s);
+// The split-T sum of a stored pass, Ypart [nsplit][B][w][NC] fp32 summed in
+// split order (fp64), packed straight into `next`'s projection (the stored
+// Y of that pass is not written), with next's tables.
+hipError_t launch_hpp_ysum_pack(const float* Ypart, int nsplit, int B, int w, int NC, const HppNext& next,
+                                hipStream_t s);
 
 // Exact squared norms: one fp64 partial per tile into partials [B][slots].
 void exact_tiles(bool bf16, bool gram, int64_t T, int64_t d, int64_t p, int32_t& tu, int32_t& tv, int32_t& slots);

@@ -26,6 +26,8 @@
 // Q, which adds nothing to the head. W3 = [Q (MP columns) | P' (m_t)].
 // The rank rule bounds the condition number of the kept columns by about
 // 1/tau, so Q is orthonormal to about (1/tau)^2 * 2^-53 ~ 1e-6 in fp64.
+#include <cstring>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -35,6 +37,7 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMaxTail = 32;
 constexpr int kGramRows = 256;   // rows of X per k_hpp_gram work group
 constexpr int kApplyRows = 64;   // rows of X per k_hpp_apply work group (4 waves x 16)
+constexpr int kMaxYCols = 32;    // columns of a stored sketch pass that k_hpp_ysum_pack takes
 
 __device__ __forceinline__ f64x4_t mfma_f64(double a, double b, f64x4_t c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -216,6 +219,81 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   return keep;
 }
 
+// ---------------------------------------------------------------------------
+// The next pass's tables and packed projection, written by the kernel that
+// produces the projection, so that pass needs no prepare launch.
+// ---------------------------------------------------------------------------
+// Record 0 and both work lists, as the prepare kernel writes them for a lone
+// layer: items1 (0, sample, row block, 0), items2 (0, sample, column block,
+// T split) with the split innermost.
+__device__ void hpp_write_tables(const HppNext& nx) {
+  for (int r = threadIdx.x; r < nx.n1; r += blockDim.x) {
+    const int i = r / nx.rbs;
+    nx.items1[r] = make_int4(0, i, r - i * nx.rbs, 0);
+  }
+  for (int r = threadIdx.x; r < nx.n2; r += blockDim.x) {
+    const int ts = r % nx.nsplit, q = r / nx.nsplit;
+    const int ub = q % nx.ubs, i = q / nx.ubs;
+    nx.items2[r] = make_int4(0, i, ub, ts);
+  }
+  if (threadIdx.x == 0) nx.recs[0] = nx.rec;
+}
+
+// The packed units of rows r0 .. r0 + 63 (r0 a multiple of 64) of sample
+// smp, from an fp32 tile in LDS (row-major, ldt floats a row): unit (ks, jb,
+// h, lane) holds rows 32 ks + 8 (lane / 16) + 0..7 of column 16 jb + lane %
+// 16, as bf16 (h = 0) or the bf16 residual (h = 1); rows past `rows` and
+// columns past `ncols` are zero. The same units the prepare kernel packs.
+__device__ void hpp_pack_tile(const float* tile, int ldt, int r0, int smp, const HppNext& nx) {
+  const int units = 2 * nx.NCB * 2 * 64;  // two K steps of 32 rows
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int lane = u & 63;
+    int q = u >> 6;
+    const int h = q & 1;
+    q >>= 1;
+    const int jb = q % nx.NCB, ks = r0 / 32 + q / nx.NCB;
+    const int c = 16 * jb + (lane & 15);
+    uint32_t b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int v = 32 * ks + 8 * (lane >> 4) + s;
+      const float x = (v < nx.rows && c < nx.ncols) ? tile[(v - r0) * ldt + c] : 0.f;
+      uint32_t hi, lo;
+      split_bf16(x, hi, lo);
+      b[s] = h ? lo : hi;
+    }
+    stg16(nx.W + smp * nx.w_stride_b + (int64_t)((ks * nx.NCB + jb) * 2 + h) * 64 + lane, pack8(b));
+  }
+}
+
+// Split-T sum of a stored pass for 64 rows of one sample (in split order,
+// fp64, rounded to fp32 as the stored Y would be), packed for the next pass.
+__global__ void __launch_bounds__(256) k_hpp_ysum_pack(const float* __restrict__ Ypart, int nsplit, int B, int w,
+                                                       int NC, HppNext nx) {
+  __shared__ float tile[64 * kMaxYCols];
+  const int i = blockIdx.y, r0 = blockIdx.x * 64;
+  const int64_t stride = (int64_t)B * w * NC;
+  const float* Y = Ypart + ((int64_t)i * w + r0) * NC;
+  for (int e = 4 * threadIdx.x; e < 64 * NC; e += 1024) {  // NC is a multiple of 16: one row per float4
+    double y[4] = {0.0, 0.0, 0.0, 0.0};
+    if (r0 + e / NC < w) {
+#pragma unroll 8
+      for (int ts = 0; ts < nsplit; ++ts) {
+        const float4 v = ldg_f32x4(Y + ts * stride + e);
+        y[0] += (double)v.x;
+        y[1] += (double)v.y;
+        y[2] += (double)v.z;
+        y[3] += (double)v.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[e + q] = (float)y[q];
+  }
+  __syncthreads();
+  hpp_pack_tile(tile, NC, r0, i, nx);
+  if (blockIdx.x == 0 && blockIdx.y == 0) hpp_write_tables(nx);
+}
+
 // Q = X Ri and P' = P - X N for kApplyRows rows (16 per wave); K slot l / 16
 // is column 4 ks + l / 16 of X. Each work group first forms its sample's
 // basis from the Gram partials itself (a few microseconds of LDS work), which
@@ -224,9 +302,10 @@ template <int MP>
 __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, int p, int mt,
                                                    const void* __restrict__ P, int ptype,
                                                    const double* __restrict__ part, int nparts, float tau,
-                                                   int32_t* rank_out, float* W3, int ldw) {
+                                                   int32_t* rank_out, float* W3, int ldw, int pack, HppNext nx) {
   constexpr int TA = MP / 16;
   __shared__ HppBasis<MP> sb;
+  __shared__ float tile[kApplyRows * (MP + kMaxTail)];   // this group's rows of W3, when packing
   const int i = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -264,12 +343,25 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = r0 + g + 4 * j;
+    if (pack) {  // for the next pass the rows go to LDS only (rows past p too; the packer zeroes them)
+      float* tr = tile + (row - blockIdx.x * kApplyRows) * ldw;
+#pragma unroll
+      for (int t = 0; t < TA; ++t) tr[16 * t + n] = (float)q[t][j];
+      if (n < mt) tr[MP + n] = (float)(pr[j][0] - pn[0][j]);
+      if (16 + n < mt) tr[MP + 16 + n] = (float)(pr[j][1] - pn[1][j]);
+      continue;
+    }
     if (row >= p) continue;
     float* wr = Wi + (int64_t)row * ldw;
 #pragma unroll
     for (int t = 0; t < TA; ++t) stg_f32(wr + 16 * t + n, (float)q[t][j]);
     if (n < mt) stg_f32(wr + MP + n, (float)(pr[j][0] - pn[0][j]));
     if (16 + n < mt) stg_f32(wr + MP + 16 + n, (float)(pr[j][1] - pn[1][j]));
+  }
+  if (pack) {  // uniform
+    __syncthreads();
+    hpp_pack_tile(tile, ldw, blockIdx.x * kApplyRows, i, nx);
+    if (blockIdx.x == 0 && blockIdx.y == 0) hpp_write_tables(nx);
   }
 }
 
@@ -282,22 +374,33 @@ size_t hpp_qr_scratch_bytes(int MP, int B, int p) {
 
 template <int MP>
 static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, char* scratch, hipStream_t s) {
+                         int ldw, int32_t* rank, char* scratch, const HppNext* next, hipStream_t s) {
   const int nparts = (p + kGramRows - 1) / kGramRows;
   double* part = (double*)scratch;
   hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  HppNext nx;
+  std::memset(&nx, 0, sizeof(nx));
+  if (next) nx = *next;
   hipLaunchKernelGGL(k_hpp_apply<MP>, dim3((p + kApplyRows - 1) / kApplyRows, B), dim3(256), 0, s, X, p, mt, P,
-                     ptype, (const double*)part, nparts, tau, rank, W3, ldw);
+                     ptype, (const double*)part, nparts, tau, rank, W3, ldw, next ? 1 : 0, nx);
   return hipGetLastError();
 }
 
 hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, void* scratch, hipStream_t s) {
-  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, s);
-  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, s);
+                         int ldw, int32_t* rank, void* scratch, const HppNext* next, hipStream_t s) {
+  if (next && (ldw > MP + kMaxTail || next->ncols > ldw || next->NCB * 16 != ldw)) return hipErrorInvalidValue;
+  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, next, s);
+  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, next, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_hpp_ysum_pack(const float* Ypart, int nsplit, int B, int w, int NC, const HppNext& next,
+                                hipStream_t s) {
+  if (NC > kMaxYCols || next.ncols > NC || next.NCB * 16 != NC || next.rows != w) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_hpp_ysum_pack, dim3((w + 63) / 64, B), dim3(256), 0, s, Ypart, nsplit, B, w, NC, next);
+  return hipGetLastError();
 }
 
 }  // namespace dpn
