@@ -44,6 +44,45 @@ __device__ __forceinline__ float w_value(const PrepLayer& P, int smp, int v, int
   return load_src(P.wsrc, row + c, P.wsrc_type);
 }
 
+// Rows v0 .. v0 + 7 of column c of sample smp's W source, zero past `rows`
+// rows or P.ncols columns. The indices are clamped into range and every load
+// is issued before any is used (a load under a per-lane condition gets a wait
+// of its own), with the source type decided once for all eight.
+__device__ __forceinline__ void w_values8(const PrepLayer& P, int smp, int v0, int c, int rows, float x[8]) {
+  const int cc = min(c, P.ncols - 1);
+  const int64_t base = smp * P.wsrc_stride_b;
+  int vr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) vr[s] = min(v0 + s, rows - 1);
+  switch (P.wsrc_type) {
+    case SRC_IDENTITY:
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[s] = v0 + s == c ? 1.f : 0.f;
+      break;
+    case SRC_SIGN: {
+      uint32_t wd[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) wd[s] = ((const uint32_t*)P.wsrc)[base + (int64_t)vr[s] * P.ld + (cc >> 5)];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[s] = ((wd[s] >> (cc & 31)) & 1u) ? -1.f : 1.f;
+      break;
+    }
+    case SRC_BF16: {
+      uint16_t hv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) hv[s] = ((const uint16_t*)P.wsrc)[base + (int64_t)vr[s] * P.ld + cc];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[s] = bf16_bits_to_f32(hv[s]);
+      break;
+    }
+    default:
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[s] = ((const float*)P.wsrc)[base + (int64_t)vr[s] * P.ld + cc];
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) x[s] = (v0 + s < rows && c < P.ncols) ? x[s] : 0.f;
+}
+
 __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
   const int first = blockIdx.x * 256;
   // the last layer whose first unit is <= first (binary search over the
@@ -78,14 +117,13 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
       const int ks = q / NCB;
       const int c = 16 * jb + (lane & 15);
       const int v0 = 32 * ks + 8 * (lane >> 4);
+      float x[8];
+      w_values8(P, smp, v0, c, rows, x);
       uint32_t b[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int v = v0 + s;
-        float x = 0.f;
-        if (v < rows && c < P.ncols) x = w_value(P, smp, v, c);
         uint32_t hi, lo;
-        split_bf16(x, hi, lo);
+        split_bf16(x[s], hi, lo);
         b[s] = h ? lo : hi;
       }
       uint4* dst = (uint4*)P.rec.W + smp * P.rec.w_stride_b;

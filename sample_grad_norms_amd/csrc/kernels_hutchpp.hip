@@ -50,10 +50,23 @@ struct HppTiles {
   static constexpr int NT = NG + 2 * TA;        // + X^T P tiles (tail columns up to 32)
 };
 
-__device__ __forceinline__ double tail_val(const void* P, int ptype, int p, int mt, int row, int t) {
-  if (row >= p || t >= mt) return 0.0;
-  if (ptype == SRC_BF16) return (double)bf16_bits_to_f32(((const uint16_t*)P)[(int64_t)row * mt + t]);
-  return (double)ldg_f32((const float*)P + (int64_t)row * mt + t);
+// Loads in these kernels are issued unconditionally from indices clamped into
+// range and the out-of-range values replaced afterwards: a load under a
+// per-lane condition gets a wait of its own, which serialises them.
+
+// Entry (row, t) of the tail projection P [p][mt], 0 outside it.
+template <bool BF16>
+__device__ __forceinline__ double tail_val(const void* P, int p, int mt, int row, int t) {
+  const int64_t off = (int64_t)min(row, p - 1) * mt + min(t, mt - 1);
+  const float v = BF16 ? bf16_bits_to_f32(((const uint16_t*)P)[off]) : ldg_f32((const float*)P + off);
+  return row < p && t < mt ? (double)v : 0.0;
+}
+
+// Entry (row, c) of X [p][MP], 0 past p rows.
+template <int MP>
+__device__ __forceinline__ double x_val(const float* Xi, int p, int row, int c) {
+  const float v = ldg_f32(Xi + (int64_t)min(row, p - 1) * MP + c);
+  return row < p ? (double)v : 0.0;
 }
 
 // Partial tiles of X^T X (upper triangle) and X^T P for kGramRows rows:
@@ -74,13 +87,21 @@ __global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, i
   for (int t = 0; t < NT; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   constexpr int U = kGramRows / 4 / 4;  // K steps per wave, loads issued together
   double xa[U][TA], pv[U][2];
+  const int row0 = s * kGramRows + 4 * wv * U + g;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int row = s * kGramRows + 4 * (wv * U + u) + g;
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int a = 0; a < TA; ++a) xa[u][a] = row < p ? (double)ldg_f32(Xi + (int64_t)row * MP + 16 * a + n) : 0.0;
-    pv[u][0] = tail_val(P, ptype, p, mt, row, n);
-    pv[u][1] = tail_val(P, ptype, p, mt, row, 16 + n);
+    for (int a = 0; a < TA; ++a) xa[u][a] = x_val<MP>(Xi, p, row0 + 4 * u, 16 * a + n);
+  if (ptype == SRC_BF16) {  // uniform
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<true>(P, p, mt, row0 + 4 * u, 16 * tt + n);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<false>(P, p, mt, row0 + 4 * u, 16 * tt + n);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -134,7 +155,9 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
     for (int s0 = 0; s0 < nparts; s0 += 8) {  // eight loads in flight, summed in part order
       double w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = s0 + u < nparts ? pi[(int64_t)(s0 + u) * NT * 256 + e] : 0.0;
+      for (int u = 0; u < 8; ++u) w[u] = pi[(int64_t)min(s0 + u, nparts - 1) * NT * 256 + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = s0 + u < nparts ? w[u] : 0.0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) v += w[u];
     }
@@ -319,12 +342,17 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
   const int arow = r0 + n;
   double xa[MP / 4], pr[4][2];
 #pragma unroll
-  for (int ks = 0; ks < MP / 4; ++ks) xa[ks] = arow < p ? (double)ldg_f32(Xi + (int64_t)arow * MP + 4 * ks + g) : 0.0;
+  for (int ks = 0; ks < MP / 4; ++ks) xa[ks] = x_val<MP>(Xi, p, arow, 4 * ks + g);
+  if (ptype == SRC_BF16) {  // uniform
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = r0 + g + 4 * j;
-    pr[j][0] = tail_val(P, ptype, p, mt, row, n);
-    pr[j][1] = tail_val(P, ptype, p, mt, row, 16 + n);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pr[j][tt] = tail_val<true>(P, p, mt, r0 + g + 4 * j, 16 * tt + n);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pr[j][tt] = tail_val<false>(P, p, mt, r0 + g + 4 * j, 16 * tt + n);
   }
   __syncthreads();
   f64x4_t q[TA], pn[2];
