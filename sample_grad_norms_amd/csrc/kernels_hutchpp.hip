@@ -332,10 +332,8 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
   const int i = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const uint32_t keep = hpp_basis<MP>(part, nparts, tau, i, sb);
-  if (blockIdx.x == 0 && tid == 0 && rank_out) rank_out[i] = __popc(keep);
-  double (&Ri)[MP][MP] = sb.Ri;
-  double (&N)[MP][kMaxTail] = sb.N;
+  // this group's rows of X and P, loaded before the basis so their latency
+  // overlaps it
   const float* Xi = X + (int64_t)i * p * MP;
   float* Wi = W3 + (int64_t)i * p * ldw;
   const int r0 = blockIdx.x * kApplyRows + 16 * wv;
@@ -354,6 +352,10 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) pr[j][tt] = tail_val<false>(P, p, mt, r0 + g + 4 * j, 16 * tt + n);
   }
+  const uint32_t keep = hpp_basis<MP>(part, nparts, tau, i, sb);
+  if (blockIdx.x == 0 && tid == 0 && rank_out) rank_out[i] = __popc(keep);
+  double (&Ri)[MP][MP] = sb.Ri;
+  double (&N)[MP][kMaxTail] = sb.N;
   __syncthreads();
   f64x4_t q[TA], pn[2];
 #pragma unroll
