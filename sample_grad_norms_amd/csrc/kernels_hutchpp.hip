@@ -149,73 +149,97 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   double (&M)[MP][kMaxTail] = sb.M;
   const int l = threadIdx.x;
   const double* pi = part + (int64_t)i * nparts * NT * 256;
-  // fixed-order sum; lane q, element j of a v_mfma_f64_16x16x4 result is (row q/16 + 4 j, column q % 16)
-  for (int e = l; e < NT * 256; e += 256) {
-    double v = 0.0;
-    for (int s0 = 0; s0 < nparts; s0 += 8) {  // eight loads in flight, summed in part order
-      double w[8];
+  // fixed-order sum over the parts (eight at a time, every tile's loads in
+  // flight together); lane q, element j of a v_mfma_f64_16x16x4 result is
+  // (row q/16 + 4 j, column q % 16); thread l holds element l of each tile
+  double v[NT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = pi[(int64_t)min(s0 + u, nparts - 1) * NT * 256 + e];
+  for (int t = 0; t < NT; ++t) v[t] = 0.0;
+  for (int s0 = 0; s0 < nparts; s0 += 8) {
+    double w[NT][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = s0 + u < nparts ? w[u] : 0.0;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v += w[u];
-    }
-    const int t = e >> 8, j = (e >> 6) & 3, q = e & 63;
+      for (int u = 0; u < 8; ++u) w[t][u] = pi[(int64_t)min(s0 + u, nparts - 1) * NT * 256 + t * 256 + l];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[t] += s0 + u < nparts ? w[t][u] : 0.0;
+  }
+  {
+    const int j = l >> 6, q = l & 63;
     const int r = (q >> 4) + 4 * j, c = q & 15;
-    if (t < NG) {
-      int a = 0, b = 0;
-      for (int aa = 0, k = 0; aa < TA; ++aa)
-        for (int bb = aa; bb < TA; ++bb, ++k)
-          if (k == t) {
-            a = aa;
-            b = bb;
-          }
-      G[16 * a + r][16 * b + c] = v;
-      G[16 * b + c][16 * a + r] = v;
-    } else {
-      const int a = (t - NG) >> 1, tt = (t - NG) & 1;
-      XP[16 * a + r][16 * tt + c] = v;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < NG) {
+        int a = 0, b = 0;
+        for (int aa = 0, k = 0; aa < TA; ++aa)
+          for (int bb = aa; bb < TA; ++bb, ++k)
+            if (k == t) {
+              a = aa;
+              b = bb;
+            }
+        G[16 * a + r][16 * b + c] = v[t];
+        G[16 * b + c][16 * a + r] = v[t];
+      } else {
+        const int a = (t - NG) >> 1, tt = (t - NG) & 1;
+        XP[16 * a + r][16 * tt + c] = v[t];
+      }
     }
   }
   __syncthreads();
 
   // Right-looking Cholesky on the Schur complement Sc (= G at the start), one
-  // entry per thread: at step j, if column j is kept, row j of R (formed only
-  // where needed) is row j of Sc times 1 / Sc[j][j]^(1/2) and every later entry (a, b) loses
-  // R[j][a] R[j][b]; so the diagonal Sc[j][j] a step reads is G[j][j] minus
-  // the squares of the kept rows above it, subtracted in row order. The same
-  // row operations on the identity give E = R^-T: row j of E is scaled by the
-  // same factor, which is kept in sj[] and applied once at the end (rows of
-  // dropped columns get 0), so a step reads only row j, which it never writes,
-  // and needs one barrier.
+  // entry per thread: at step j the pivot is d_j = Sc[j][j]; if column j is
+  // kept, row j of R is row j of Sc over d_j^(1/2) and every later entry
+  // (a, b) loses Sc[j][a] Sc[j][b] / d_j, so the d_j a step reads is G[j][j]
+  // minus the squares of the kept rows above it, subtracted in row order.
+  // The same row operations on the identity give E = R^-T with its rows left
+  // unscaled: row j is scaled by d_j^(-1/2) once at the end (rows of dropped
+  // columns by 0). A step reads only row j, which it never writes, so it
+  // needs one barrier; a thread reads its operands of row j together with
+  // the pivot, and the square roots wait until after the loop (Sc[j][j] keeps
+  // d_j, since later steps change only entries below and right of it).
+  // Column j is kept when d_j^(1/2) > tau max_a ||x_a||, compared as squares.
   double (&Sc)[MP][MP] = G;
   double (&E)[MP][MP] = Ri;
   double (&sj)[MP] = sb.sj;
+  constexpr int EPT = MP * MP / 256;   // entries per thread
   for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
   double dmax = 0.0;
   for (int j = 0; j < MP; ++j) dmax = fmax(dmax, Sc[j][j]);
-  const double scale = sqrt(fmax(dmax, 0.0));
+  const double thr = (double)tau * sqrt(fmax(dmax, 0.0));
+  const double thr2 = thr * thr;
   __syncthreads();
   uint32_t keep = 0;
   for (int j = 0; j < MP; ++j) {
-    const double nj = sqrt(fmax(Sc[j][j], 0.0));
-    const bool kept = nj > (double)tau * scale && nj > 0.0;   // uniform
-    const double inv = kept ? 1.0 / nj : 0.0;
-    if (kept) keep |= 1u << j;
-    if (l == 0) sj[j] = inv;
+    const double dj = Sc[j][j];
+    double sjr[EPT], sjc[EPT], ejc[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = l + 256 * u, r = e / MP, c = e % MP;
+      sjr[u] = Sc[j][r];
+      sjc[u] = Sc[j][c];
+      ejc[u] = E[j][c];
+    }
+    const bool kept = dj > 0.0 && dj > thr2;   // uniform
     if (kept) {
-      for (int e = l; e < MP * MP; e += 256) {
-        const int r = e / MP, c = e % MP;
+      keep |= 1u << j;
+      const double inv = 1.0 / dj;
+#pragma unroll
+      for (int u = 0; u < EPT; ++u) {
+        const int e = l + 256 * u, r = e / MP, c = e % MP;
         if (r > j) {
-          const double rr = Sc[j][r] * inv;                   // R[j][r]
-          if (c > j) Sc[r][c] -= rr * (Sc[j][c] * inv);
-          E[r][c] -= rr * (E[j][c] * inv);
+          const double f = sjr[u] * inv;
+          if (c > j) Sc[r][c] -= f * sjc[u];
+          E[r][c] -= f * ejc[u];
         }
       }
     }
     __syncthreads();
   }
+  if (l < MP) sj[l] = (keep >> l) & 1u ? 1.0 / sqrt(Sc[l][l]) : 0.0;
+  __syncthreads();
   for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] *= sj[e / MP];
   __syncthreads();
   // Ri = E^T, back into Ri's storage (E aliases it): transpose via R (scratch)
@@ -224,18 +248,36 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   for (int e = l; e < MP * MP; e += 256) (&Ri[0][0])[e] = (&R[0][0])[e];
   __syncthreads();
   // M[c][t] = sum_a Ri[a][c] XP[a][t]
+  // (both sums run over the triangle of Ri in index order; every operand is
+  // read before the first product)
   for (int e = l; e < MP * kMaxTail; e += 256) {
     const int c = e / kMaxTail, t = e % kMaxTail;
+    double ra[MP], xa[MP];
+#pragma unroll
+    for (int a = 0; a < MP; ++a) {
+      ra[a] = Ri[a][c];
+      xa[a] = XP[a][t];
+    }
     double v = 0.0;
-    for (int a = 0; a <= c; ++a) v += Ri[a][c] * XP[a][t];
+#pragma unroll
+    for (int a = 0; a < MP; ++a)
+      if (a <= c) v += ra[a] * xa[a];
     M[c][t] = v;
   }
   __syncthreads();
   // N[a][t] = sum_c Ri[a][c] M[c][t]
   for (int e = l; e < MP * kMaxTail; e += 256) {
     const int a = e / kMaxTail, t = e % kMaxTail;
+    double ra[MP], mc[MP];
+#pragma unroll
+    for (int c = 0; c < MP; ++c) {
+      ra[c] = Ri[a][c];
+      mc[c] = M[c][t];
+    }
     double v = 0.0;
-    for (int c = a; c < MP; ++c) v += Ri[a][c] * M[c][t];
+#pragma unroll
+    for (int c = 0; c < MP; ++c)
+      if (c >= a) v += ra[c] * mc[c];
     sb.N[a][t] = v;
   }
   __syncthreads();
