@@ -138,7 +138,9 @@ dpnorm_status dpnorm_exact_workspace(dpnorm_dtype dt, int64_t B, int64_t T, int6
  * P [p][k] shared by the samples (caller draws N(0, 1/k) entries;
  * 1 <= k <= 64).
  * accumulate = 0 writes n[i] = n_hat_i; accumulate = 1 adds: n[i] += n_hat_i.
- * A, G, P, n device pointers; n must not overlap A, G, P or ws. */
+ * A, G, P, n device pointers; n must not overlap A, G, P or ws. A bf16 P
+ * with k = 16, 32 or 64 that is 16-byte aligned is read in place (one launch
+ * fewer than the packed copy other P take; the results are the same). */
 dpnorm_status dpnorm_hutch(const void* A, const void* G, const void* P, dpnorm_dtype dt, int64_t B,
                            int64_t T, int64_t d, int64_t p, int64_t k, float* n, int accumulate,
                            void* ws, size_t ws_bytes, hipStream_t stream);

@@ -303,6 +303,22 @@ void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base,
   P.layer = e;
 }
 
+bool aligned(const void* p, size_t a);
+
+// A pass over one layer whose W is the caller's bf16 [w1][16 NCB] matrix
+// (16-byte aligned, shared by the batch) runs its stages in implicit mode:
+// the layer's record travels in the launch arguments, the work items are
+// derived from their indices and stage 1 reads W as it is, so the pass
+// launches no prepare kernel.
+bool implicit_pass(const PassPlan& pl, const std::vector<PassLayer>& L) {
+  if (!pl.bf16 || pl.HL != 1 || L.size() != 1 || pl.entries.size() != 1 || pl.groups.size() != 1 ||
+      pl.class_ncb.size() != 1 || pl.groups[0].ncb != pl.NCB)
+    return false;
+  const PassLayer& in = L[0];
+  return in.wsrc_type == SRC_BF16 && in.nsamples == 1 && in.ld == 16 * pl.NCB && in.ncols == 16 * pl.NCB &&
+         in.wsrc != nullptr && aligned(in.wsrc, 16);
+}
+
 // prepare = false: the tables and packed W are already in place (written by
 // the kernel that produced W); ysum = false: the split-T partial tiles are
 // left for the caller to reduce.
@@ -312,7 +328,8 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   LayerRec* recs = (LayerRec*)(base + pl.off_recs);
   int4* items1 = (int4*)(base + pl.off_items1);
   int4* items2 = (int4*)(base + pl.off_items2);
-  for (int c0 = 0; prepare && c0 < entries; c0 += kPrepChunk) {
+  const bool impl = prepare && implicit_pass(pl, L);
+  for (int c0 = 0; prepare && !impl && c0 < entries; c0 += kPrepChunk) {
     PrepArgs a;
     std::memset(&a, 0, sizeof(a));
     a.recs = recs;
@@ -337,6 +354,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
     DPN_TRY(tr.mark(DPNORM_KERNEL_PREPARE));
   }
   StageArgs st;
+  std::memset(&st, 0, sizeof(st));
   st.recs = recs;
   st.B = (int32_t)pl.B;
   st.T = (int32_t)pl.T;
@@ -345,18 +363,27 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   st.slots_per_sample = pl.slots;
   st.partials = (double2*)(base + pl.off_partials);
 
+  if (impl) {
+    PrepLayer P;
+    fill_entry(pl, L, base, 0, P);
+    st.rec0 = P.rec;
+    st.rec0.W = L[0].wsrc;
+    st.rbs = pl.rbs;
+    st.ubs = pl.groups[0].ubs;
+  }
+
   st.items = items1;
   st.n_items = (int32_t)pl.total1;
-  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, s));
+  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, impl, s));
   DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
 
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {
     st.items = items2 + pl.class_begin[c];
     st.n_items = pl.class_end[c] - pl.class_begin[c];
-    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.direct(), s));
+    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.direct(), impl, s));
     DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
     if (pl.needs_ysum() && ysum) {
-      DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, s));
+      DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, impl, s));
       DPN_TRY(tr.mark(DPNORM_KERNEL_YSUM));
     }
   }

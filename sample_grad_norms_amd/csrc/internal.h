@@ -82,18 +82,26 @@ struct StageArgs {
   int32_t B, T, Tpad, nsplit;
   int32_t slots_per_sample;
   double2* partials;       // [B][slots] (sum of squares below / above split)
+  // Implicit mode (a call over one layer, bf16, with a [w1][16 NCB] bf16 W
+  // read as it is): no record or item table in memory; the layer is rec0
+  // (rec0.W the caller's W) and item b is derived from b: stage 1
+  // (0, b / rbs, b % rbs, 0), stage 2 (0, sample, column block, split) with
+  // the split innermost and ubs column blocks per sample.
+  LayerRec rec0;
+  int32_t rbs, ubs;
 };
 
 // mode for stage 2 and the split-T reduction
 enum Mode : int32_t { MODE_SQ = 0, MODE_STORE = 1 };
 
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, hipStream_t s);
+// implicit: the stages run in implicit mode (bf16, HL == 1 only)
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool implicit, hipStream_t s);
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).
-hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s);
-hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s);
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, bool implicit, hipStream_t s);
+hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, bool implicit, hipStream_t s);
 // work groups of the split-T reduction per (layer, sample, column block)
 inline int ysum_chunks(int cols_per_block, int NCB) { return (cols_per_block * 16 * NCB + kYsumChunk - 1) / kYsumChunk; }
 // n (+)= scale * (sum of both partial sums); head / tail get the scaled sums.

@@ -183,22 +183,54 @@ __global__ void __launch_bounds__(256) k_prepare(PrepArgs a) {
 // starts 41 stages apart (modulo the stage count).
 // V layout: [B][Tpad/32][NCB][2][64] uint4.
 // ---------------------------------------------------------------------------
+// Work items and the layer record: from the tables, or in implicit mode
+// (one layer; StageArgs::rec0) derived from the item index.
+template <bool IMPL>
+__device__ __forceinline__ int4 stage1_item(const StageArgs& a, uint32_t b) {
+  if (IMPL) {
+    const int i = (int)b / a.rbs;
+    return make_int4(0, i, (int)b - i * a.rbs, 0);
+  }
+  return a.items[b];
+}
+template <bool IMPL>
+__device__ __forceinline__ int4 stage2_item(const StageArgs& a, int b) {
+  if (IMPL) {
+    const int ts = b % a.nsplit, q = b / a.nsplit;
+    return make_int4(0, q / a.ubs, q % a.ubs, ts);
+  }
+  return a.items[b];
+}
+template <bool IMPL>
+__device__ __forceinline__ const LayerRec* layer_rec(const StageArgs& a, int layer) {
+  return IMPL ? &a.rec0 : a.recs + layer;
+}
+
+__device__ __attribute__((aligned(16))) uint4 g_zero16[1];   // 16 zero bytes (static storage)
+
 constexpr int kK1Cols = 64;                          // columns of X1 per stage (one 128-byte line)
 constexpr int kK1XDma = 32 * kK1Cols * 2 / 1024;     // 1 KB X1 instructions per wave per stage (its 32 rows)
 constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
 
 // NW waves, 32 NW rows per item: 4 (128 rows) normally, 2 (64 rows) when
 // 128-row items would leave CUs idle.
-template <int NCB, int HL, int NW>
+// IMPL (implicit mode, HL = 1): W is the caller's bf16 [w1][NC] matrix. A
+// stage's 64 rows of it are one contiguous run, loaded as they are (rows
+// past w1 from a zero row) and kept row-major in LDS; each B operand is two
+// transposing reads (rows 32 kk + 8 g .. + 3 and + 4 .. + 7 of column
+// 16 jb + n), so the call needs no packed copy of W.
+template <int NCB, int HL, int NW, bool IMPL>
 __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
+  static_assert(!IMPL || HL == 1, "implicit mode reads a bf16 W");
+  constexpr int NC = 16 * NCB;
   constexpr int kRows = 32 * NW;
   constexpr int kK1XBytes = kRows * kK1Cols * 2;         // X1 bytes per stage (16 KB for 4 waves)
   constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per stage
   constexpr int kStage = kK1XBytes + kWBlocks * 1024;
   constexpr int kPerWave = kK1XDma + kWBlocks / NW;      // loads every wave issues per stage (at least)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kK1Bufs * kStage];
-  const int4 it = a.items[blockIdx.x];
-  const LayerRec* L = a.recs + it.x;
+  const int4 it = stage1_item<IMPL>(a, blockIdx.x);
+  const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, rb = it.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -206,6 +238,7 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   const int r0 = rb * kRows;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
   const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
+  const uint16_t* Wr = (const uint16_t*)L->W;                       // IMPL: [w][NC] as the caller holds it
   const int nst = (w + kK1Cols - 1) / kK1Cols;
   const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nst);  // first column stage of this group
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
@@ -232,7 +265,16 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int m0 = 0; m0 < (kWBlocks + NW - 1) / NW; ++m0) {
       const int m = NW * m0 + wv;
-      if (m < kWBlocks) dma16(Wp + ((int64_t)cst * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
+      if (IMPL) {  // instruction m: rows 64 cst + (512 / NC) m .., 2 NCB lanes of 16 bytes a row
+        if (m < kWBlocks) {
+          const int row = 64 * cst + m * (512 / NC) + lane / (2 * NCB);
+          const void* src =
+              row < w ? (const void*)(Wr + (int64_t)row * NC + 8 * (lane % (2 * NCB))) : (const void*)g_zero16;
+          dma16(src, buf + (uint32_t)(kK1XBytes + m * 1024));
+        }
+      } else if (m < kWBlocks) {
+        dma16(Wp + ((int64_t)cst * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
+      }
     }
   };
 
@@ -259,10 +301,20 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       uint4 f[NCB][HL];
+      if (IMPL) {
+        const unsigned char* wr = buf + kK1XBytes + (32 * kk + 8 * g + (n >> 2)) * (NC * 2) + (n & 3) * 8;
 #pragma unroll
-      for (int jb = 0; jb < NCB; ++jb)
+        for (int jb = 0; jb < NCB; ++jb) {
+          const uint2 lo = lds_read_tr16(wr + 32 * jb);
+          const uint2 hi = lds_read_tr16(wr + 4 * (NC * 2) + 32 * jb);
+          f[jb][0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      } else {
 #pragma unroll
-        for (int h = 0; h < HL; ++h) f[jb][h] = wf[((kk * NCB + jb) * HL + h) * 64];
+        for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+          for (int h = 0; h < HL; ++h) f[jb][h] = wf[((kk * NCB + jb) * HL + h) * 64];
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int row = 32 * wv + 16 * mt + n;
@@ -416,7 +468,7 @@ constexpr int kK2Rows = 32;                              // rows of X2 per stage
 constexpr int kK2XBytes = kK2Rows * kColsK2Bf16 * 2;     // X2 bytes per stage (32 KB)
 
 
-template <int NCB, bool DIRECT>
+template <int NCB, bool DIRECT, bool IMPL>
 __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
   constexpr int kVBlocks = 2 * NCB;                      // 1 KB V fragment blocks per chunk
   constexpr int kStage = kK2XBytes + kVBlocks * 1024;
@@ -424,8 +476,8 @@ __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
   constexpr int kXDma = kK2Rows / 4;                     // 1 KB X2 rows per wave per stage
   constexpr int kP = kXDma + kVBlocks / 4;               // loads every wave issues per stage (at least)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
-  const int4 it = a.items[xcd_item(blockIdx.x, (uint32_t)a.n_items)];
-  const LayerRec* L = a.recs + it.x;
+  const int4 it = stage2_item<IMPL>(a, xcd_item(blockIdx.x, (uint32_t)a.n_items));
+  const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, ub = it.z, ts = it.w;
   const int w = L->w2, T = a.T;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -551,11 +603,11 @@ __global__ void __launch_bounds__(256) k_tcontract_f32(StageArgs a) {
 // flight at a time), then either squares and reduces into the wave's own
 // partial slot (MODE_SQ) or stores Y (MODE_STORE).
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, bool IMPL>
 __global__ void __launch_bounds__(64) k_ysum(StageArgs a, int NC, int cols_per_block, int ychunks) {
   const int blk = blockIdx.x / ychunks, chunk = blockIdx.x - blk * ychunks;
-  const int4 it = a.items[(int64_t)blk * a.nsplit];
-  const LayerRec* L = a.recs + it.x;
+  const int4 it = stage2_item<IMPL>(a, blk * a.nsplit);
+  const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, ub = it.z;
   const int w = L->w2;
   const int u0 = ub * cols_per_block;
@@ -654,25 +706,30 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
 }
 
 template <int NW>
-static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, hipStream_t s) {
+static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, bool implicit, hipStream_t s) {
   const dim3 grid(a.n_items), blk(64 * NW);
-  if (HL == 1) {
-    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW>), grid, blk, 0, s, a);
-    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW>), grid, blk, 0, s, a);
+  if (implicit) {
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW, true>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW, true>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW, true>), grid, blk, 0, s, a);
+  } else if (HL == 1) {
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW, false>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW, false>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW, false>), grid, blk, 0, s, a);
   } else {
-    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2, NW>), grid, blk, 0, s, a);
-    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2, NW>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_rowproj_bf16<4, 2, NW>), grid, blk, 0, s, a);
+    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2, NW, false>), grid, blk, 0, s, a);
+    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2, NW, false>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_rowproj_bf16<4, 2, NW, false>), grid, blk, 0, s, a);
   }
 }
 
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, hipStream_t s) {
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool implicit, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
+  if (implicit && (!bf16 || HL != 1 || a.rbs < 1)) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
   if (bf16) {
-    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, s);
-    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, s);
+    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, implicit, s);
+    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, implicit, s);
     else return hipErrorInvalidValue;
   } else {
     if (rows1 != kRowsK1) return hipErrorInvalidValue;
@@ -683,20 +740,30 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
   return hipGetLastError();
 }
 
-hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, hipStream_t s) {
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, bool implicit, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
+  if (implicit && (!bf16 || a.ubs < 1 || (NCB != 1 && NCB != 2 && NCB != 4))) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
 #define DPN_TC(KER, N)                                                          \
   do {                                                                          \
     if (direct) hipLaunchKernelGGL((KER<N, true>), grid, blk, 0, s, a);         \
     else hipLaunchKernelGGL((KER<N, false>), grid, blk, 0, s, a);               \
   } while (0)
-  if (bf16) {
-    if (NCB == 1) DPN_TC(k_tcontract_bf16, 1);
-    else if (NCB == 2) DPN_TC(k_tcontract_bf16, 2);
-    else if (NCB == 3) DPN_TC(k_tcontract_bf16, 3);
-    else if (NCB == 4) DPN_TC(k_tcontract_bf16, 4);
-    else DPN_TC(k_tcontract_bf16, 6);
+#define DPN_TCB(N, I)                                                                         \
+  do {                                                                                        \
+    if (direct) hipLaunchKernelGGL((k_tcontract_bf16<N, true, I>), grid, blk, 0, s, a);       \
+    else hipLaunchKernelGGL((k_tcontract_bf16<N, false, I>), grid, blk, 0, s, a);             \
+  } while (0)
+  if (bf16 && implicit) {
+    if (NCB == 1) DPN_TCB(1, true);
+    else if (NCB == 2) DPN_TCB(2, true);
+    else DPN_TCB(4, true);
+  } else if (bf16) {
+    if (NCB == 1) DPN_TCB(1, false);
+    else if (NCB == 2) DPN_TCB(2, false);
+    else if (NCB == 3) DPN_TCB(3, false);
+    else if (NCB == 4) DPN_TCB(4, false);
+    else DPN_TCB(6, false);
   } else {
     if (NCB == 1) DPN_TC(k_tcontract_f32, 1);
     else if (NCB == 2) DPN_TC(k_tcontract_f32, 2);
@@ -705,18 +772,24 @@ hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct,
     else DPN_TC(k_tcontract_f32, 4);
   }
 #undef DPN_TC
+#undef DPN_TCB
   return hipGetLastError();
 }
 
-hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, hipStream_t s) {
+hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, bool implicit, hipStream_t s) {
   const int blocks = a.n_items / a.nsplit;
   const int ychunks = ysum_chunks(cols_per_block, NCB);
   if (blocks <= 0) return hipSuccess;
+  if (implicit && a.ubs < 1) return hipErrorInvalidValue;
   const dim3 grid(blocks * ychunks);
-  if (mode == MODE_SQ)
-    hipLaunchKernelGGL(k_ysum<MODE_SQ>, grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+  if (mode == MODE_SQ && implicit)
+    hipLaunchKernelGGL((k_ysum<MODE_SQ, true>), grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+  else if (mode == MODE_SQ)
+    hipLaunchKernelGGL((k_ysum<MODE_SQ, false>), grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+  else if (implicit)
+    hipLaunchKernelGGL((k_ysum<MODE_STORE, true>), grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   else
-    hipLaunchKernelGGL(k_ysum<MODE_STORE>, grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
+    hipLaunchKernelGGL((k_ysum<MODE_STORE, false>), grid, dim3(64), 0, s, a, 16 * NCB, cols_per_block, ychunks);
   return hipGetLastError();
 }
 

@@ -131,6 +131,26 @@ def test_deterministic_bitwise():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B,T,d,p,k", [(3, 333, 1032, 520, 32), (32, 1000, 264, 136, 32), (4, 200, 136, 64, 64),
+                                       (2, 128, 2048, 512, 16)])
+def test_projection_read_in_place_matches_packed_copy(B, T, d, p, k):
+    """A single-layer bf16 call whose P is 16-byte aligned with k = 16, 32 or
+    64 reads P in place; the same values 2 bytes further on take the packed
+    path. Both feed the MFMAs the same operands, so the results agree bitwise
+    (rows of P past the last full 64-row stage come from a zero row)."""
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(B, T, d, p, k, seed=B + T + k, device=dev(), dtype=torch.bfloat16)
+    buf = torch.empty(p * k + 8, dtype=torch.bfloat16, device=dev())
+    buf[1:1 + p * k].copy_(prob.P.reshape(-1))
+    p_shifted = buf[1:1 + p * k].view(p, k)
+    assert prob.P.data_ptr() % 16 == 0 and p_shifted.data_ptr() % 16 != 0
+    a = dp.hutch(prob.A, prob.G, prob.P)
+    b = dp.hutch(prob.A, prob.G, p_shifted)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    check(a.cpu(), oracle.hutch(prob.A, prob.G, prob.P), 1e-3, f"in place B{B} T{T} d{d} p{p} k{k}")
+
+
 def test_clip_factor_kernel_special_values():
     import sample_grad_norms_amd as dp
     n = torch.tensor([0.0, float("inf"), float("nan"), 4.0, 16.0, 1.0, 64.0, 1e-30], device=dev())
