@@ -255,8 +255,10 @@ struct Tracer {
   } while (0)
 
 // Prepare-table entry e of a pass (pl.entries): its record and what the
-// prepare kernel derives from it. The record of entry e is recs[e].
-void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, int e, PrepLayer& P) {
+// prepare kernel derives from it. The record of entry e is recs[e]. raw:
+// stage 1 reads the layer's W in place (no packing units).
+void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base, int e, PrepLayer& P,
+                bool raw = false) {
   std::memset(&P, 0, sizeof(P));
   LayerRec& R = P.rec;
   R.split = 1 << 30;
@@ -265,7 +267,7 @@ void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base,
     const PassLayer& in = L[le];
     const PassGroup& g = pl.groups[pl.group_of[le]];
     R.X1 = in.X1;
-    R.W = base + pl.off_W[le];
+    R.W = raw ? in.wsrc : base + pl.off_W[le];
     R.w_stride_b = in.nsamples > 1 ? (int64_t)packed_units(pl, in.w1) : 0;
     R.w1 = (int32_t)in.w1;
     if (pl.bf16) {
@@ -281,7 +283,7 @@ void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base,
     P.ld = (int32_t)in.ld;
     P.ncols = in.ncols;
     P.nsamples = in.nsamples;
-    P.n_pack = pl.n_pack[le];
+    P.n_pack = raw ? 0 : pl.n_pack[le];
     P.k1_begin = pl.k1_begin[le];
     P.n1 = pl.n1[le];
   }
@@ -305,18 +307,24 @@ void fill_entry(const PassPlan& pl, const std::vector<PassLayer>& L, char* base,
 
 bool aligned(const void* p, size_t a);
 
-// A pass over one layer whose W is the caller's bf16 [w1][16 NCB] matrix
-// (16-byte aligned, shared by the batch) runs its stages in implicit mode:
-// the layer's record travels in the launch arguments, the work items are
-// derived from their indices and stage 1 reads W as it is, so the pass
-// launches no prepare kernel.
+// Stage 1 reads every layer's W in place when each is the caller's bf16
+// [w1][16 NCB] matrix, 16-byte aligned and shared by the batch: the prepare
+// kernel then only writes the records and item lists.
+bool raw_pass(const PassPlan& pl, const std::vector<PassLayer>& L) {
+  if (!pl.bf16 || pl.HL != 1 || L.empty()) return false;
+  for (const PassLayer& in : L)
+    if (in.wsrc_type != SRC_BF16 || in.nsamples != 1 || in.ld != 16 * pl.NCB || in.ncols != 16 * pl.NCB ||
+        in.wsrc == nullptr || !aligned(in.wsrc, 16))
+      return false;
+  return true;
+}
+
+// Such a pass over one layer runs its stages in implicit mode: the layer's
+// record travels in the launch arguments and the work items are derived from
+// their indices, so the pass launches no prepare kernel at all.
 bool implicit_pass(const PassPlan& pl, const std::vector<PassLayer>& L) {
-  if (!pl.bf16 || pl.HL != 1 || L.size() != 1 || pl.entries.size() != 1 || pl.groups.size() != 1 ||
-      pl.class_ncb.size() != 1 || pl.groups[0].ncb != pl.NCB)
-    return false;
-  const PassLayer& in = L[0];
-  return in.wsrc_type == SRC_BF16 && in.nsamples == 1 && in.ld == 16 * pl.NCB && in.ncols == 16 * pl.NCB &&
-         in.wsrc != nullptr && aligned(in.wsrc, 16);
+  return L.size() == 1 && pl.entries.size() == 1 && pl.groups.size() == 1 && pl.class_ncb.size() == 1 &&
+         pl.groups[0].ncb == pl.NCB && raw_pass(pl, L);
 }
 
 // prepare = false: the tables and packed W are already in place (written by
@@ -328,7 +336,8 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   LayerRec* recs = (LayerRec*)(base + pl.off_recs);
   int4* items1 = (int4*)(base + pl.off_items1);
   int4* items2 = (int4*)(base + pl.off_items2);
-  const bool impl = prepare && implicit_pass(pl, L);
+  const bool raw = prepare && raw_pass(pl, L);
+  const bool impl = raw && implicit_pass(pl, L);
   for (int c0 = 0; prepare && !impl && c0 < entries; c0 += kPrepChunk) {
     PrepArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -344,7 +353,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
     const int cn = std::min(kPrepChunk, entries - c0);
     for (int j = 0; j < cn; ++j) {
       PrepLayer& P = a.L[j];
-      fill_entry(pl, L, base, c0 + j, P);
+      fill_entry(pl, L, base, c0 + j, P, raw);
       P.unit_begin = units;
       units += (P.n_pack + P.n1 + P.n2 + 1 + 255) / 256 * 256;  // next entry starts a work group
     }
@@ -365,16 +374,15 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
 
   if (impl) {
     PrepLayer P;
-    fill_entry(pl, L, base, 0, P);
+    fill_entry(pl, L, base, 0, P, true);
     st.rec0 = P.rec;
-    st.rec0.W = L[0].wsrc;
     st.rbs = pl.rbs;
     st.ubs = pl.groups[0].ubs;
   }
 
   st.items = items1;
   st.n_items = (int32_t)pl.total1;
-  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, impl, s));
+  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, raw, impl, s));
   DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
 
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {

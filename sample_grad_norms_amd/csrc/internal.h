@@ -95,8 +95,11 @@ struct StageArgs {
 enum Mode : int32_t { MODE_SQ = 0, MODE_STORE = 1 };
 
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
-// implicit: the stages run in implicit mode (bf16, HL == 1 only)
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool implicit, hipStream_t s);
+// raw: every record's W is the caller's bf16 [w1][16 NCB] matrix, read in
+// place (bf16, HL == 1 only); implicit: the stages run in implicit mode
+// (which reads W in place too).
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool raw, bool implicit,
+                          hipStream_t s);
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).

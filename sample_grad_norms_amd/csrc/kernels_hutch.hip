@@ -214,14 +214,16 @@ constexpr int kK1Bufs = 4;                           // LDS ring: three stages i
 
 // NW waves, 32 NW rows per item: 4 (128 rows) normally, 2 (64 rows) when
 // 128-row items would leave CUs idle.
-// IMPL (implicit mode, HL = 1): W is the caller's bf16 [w1][NC] matrix. A
-// stage's 64 rows of it are one contiguous run, loaded as they are (rows
-// past w1 from a zero row) and kept row-major in LDS; each B operand is two
-// transposing reads (rows 32 kk + 8 g .. + 3 and + 4 .. + 7 of column
-// 16 jb + n), so the call needs no packed copy of W.
-template <int NCB, int HL, int NW, bool IMPL>
+// RAW (HL = 1): W is the caller's bf16 [w1][NC] matrix. A stage's 64 rows
+// of it are one contiguous run, loaded as they are (rows past w1 from a zero
+// row) and kept row-major in LDS; each B operand is two transposing reads
+// (rows 32 kk + 8 g .. + 3 and + 4 .. + 7 of column 16 jb + n), so the call
+// needs no packed copy of W. IMPL: implicit mode (items and record not in
+// memory; always RAW).
+template <int NCB, int HL, int NW, bool RAW, bool IMPL>
 __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
-  static_assert(!IMPL || HL == 1, "implicit mode reads a bf16 W");
+  static_assert(!RAW || HL == 1, "W read in place is bf16");
+  static_assert(!IMPL || RAW, "implicit mode reads W in place");
   constexpr int NC = 16 * NCB;
   constexpr int kRows = 32 * NW;
   constexpr int kK1XBytes = kRows * kK1Cols * 2;         // X1 bytes per stage (16 KB for 4 waves)
@@ -238,7 +240,7 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   const int r0 = rb * kRows;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
   const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
-  const uint16_t* Wr = (const uint16_t*)L->W;                       // IMPL: [w][NC] as the caller holds it
+  const uint16_t* Wr = (const uint16_t*)L->W;                       // RAW: [w][NC] as the caller holds it
   const int nst = (w + kK1Cols - 1) / kK1Cols;
   const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nst);  // first column stage of this group
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
@@ -265,7 +267,7 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int m0 = 0; m0 < (kWBlocks + NW - 1) / NW; ++m0) {
       const int m = NW * m0 + wv;
-      if (IMPL) {  // instruction m: rows 64 cst + (512 / NC) m .., 2 NCB lanes of 16 bytes a row
+      if (RAW) {  // instruction m: rows 64 cst + (512 / NC) m .., 2 NCB lanes of 16 bytes a row
         if (m < kWBlocks) {
           const int row = 64 * cst + m * (512 / NC) + lane / (2 * NCB);
           const void* src =
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       uint4 f[NCB][HL];
-      if (IMPL) {
+      if (RAW) {
         const unsigned char* wr = buf + kK1XBytes + (32 * kk + 8 * g + (n >> 2)) * (NC * 2) + (n & 3) * 8;
 #pragma unroll
         for (int jb = 0; jb < NCB; ++jb) {
@@ -705,31 +707,31 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NW>
-static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, bool implicit, hipStream_t s) {
+template <int NW, int HL, bool RAW, bool IMPL>
+static void rowproj_bf16_ncb(const StageArgs& a, int NCB, hipStream_t s) {
   const dim3 grid(a.n_items), blk(64 * NW);
-  if (implicit) {
-    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW, true>), grid, blk, 0, s, a);
-    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW, true>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW, true>), grid, blk, 0, s, a);
-  } else if (HL == 1) {
-    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 1, NW, false>), grid, blk, 0, s, a);
-    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 1, NW, false>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_rowproj_bf16<4, 1, NW, false>), grid, blk, 0, s, a);
-  } else {
-    if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, 2, NW, false>), grid, blk, 0, s, a);
-    else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, 2, NW, false>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_rowproj_bf16<4, 2, NW, false>), grid, blk, 0, s, a);
-  }
+  if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
+  else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
+  else hipLaunchKernelGGL((k_rowproj_bf16<4, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
 }
 
-hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool implicit, hipStream_t s) {
+template <int NW>
+static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, bool raw, bool implicit, hipStream_t s) {
+  if (implicit) rowproj_bf16_ncb<NW, 1, true, true>(a, NCB, s);
+  else if (raw) rowproj_bf16_ncb<NW, 1, true, false>(a, NCB, s);
+  else if (HL == 1) rowproj_bf16_ncb<NW, 1, false, false>(a, NCB, s);
+  else rowproj_bf16_ncb<NW, 2, false, false>(a, NCB, s);
+}
+
+hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool raw, bool implicit,
+                          hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
-  if (implicit && (!bf16 || HL != 1 || a.rbs < 1)) return hipErrorInvalidValue;
+  if ((raw || implicit) && (!bf16 || HL != 1)) return hipErrorInvalidValue;
+  if (implicit && a.rbs < 1) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
   if (bf16) {
-    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, implicit, s);
-    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, implicit, s);
+    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, raw, implicit, s);
+    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, raw, implicit, s);
     else return hipErrorInvalidValue;
   } else {
     if (rows1 != kRowsK1) return hipErrorInvalidValue;
