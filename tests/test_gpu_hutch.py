@@ -151,6 +151,30 @@ def test_projection_read_in_place_matches_packed_copy(B, T, d, p, k):
     check(a.cpu(), oracle.hutch(prob.A, prob.G, prob.P), 1e-3, f"in place B{B} T{T} d{d} p{p} k{k}")
 
 
+def test_grouped_projection_read_in_place_matches_packed_copy():
+    """Grouped bf16 calls read every P in place when all are 16-byte aligned
+    with 16, 32 or 64 columns (the prepare kernel then writes only tables);
+    one P shifted by 2 bytes sends the whole call through packed copies. The
+    MFMA operands are the same, so the sums agree bitwise."""
+    import sample_grad_norms_amd as dp
+    B, T, k = 2, 700, 32
+    layers, shifted = [], []
+    for j, (d, p) in enumerate(((264, 136), (128, 520), (1032, 64))):
+        pr = workloads.random_problem(B, T, d, p, k, seed=50 + j, device=dev(), dtype=torch.bfloat16)
+        layers.append((pr.A, pr.G, pr.P))
+        shifted.append((pr.A, pr.G, pr.P))
+    p0 = layers[0][2]
+    buf = torch.empty(p0.numel() + 8, dtype=torch.bfloat16, device=dev())
+    buf[1:1 + p0.numel()].copy_(p0.reshape(-1))
+    shifted[0] = (layers[0][0], layers[0][1], buf[1:1 + p0.numel()].view(p0.shape))
+    a = dp.hutch_grouped(layers)
+    b = dp.hutch_grouped(shifted)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    want = sum(oracle.hutch(A, G, P) for A, G, P in layers)
+    check(a.cpu(), want, 1e-3, "grouped, P in place")
+
+
 def test_clip_factor_kernel_special_values():
     import sample_grad_norms_amd as dp
     n = torch.tensor([0.0, float("inf"), float("nan"), 4.0, 16.0, 1.0, 64.0, 1e-30], device=dev())
