@@ -20,7 +20,7 @@ constexpr int kRowsK1Small = 64;  // same with 2 waves (bf16, when 128-row items
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 256;   // elements of a Y tile per split-T reduction work group (one wave)
-constexpr int kPrepChunk = 48;    // layers described per prepare launch (a ~7 KB kernel-argument table)
+constexpr int kPrepChunk = 160;   // layers described per prepare launch (a ~24 KB kernel-argument table; one launch covers a 1B-class model)
 
 // SIGN: bit-packed +-1, ld in 32-bit words; IDENTITY: W = I (no source array)
 enum SrcType : int32_t { SRC_F32 = 0, SRC_BF16 = 1, SRC_SIGN = 2, SRC_IDENTITY = 3 };
