@@ -7,8 +7,10 @@
 // groups, so Hutch++ gets its head and tail from one pass) or by storing Y_i.
 // For the Hutchinson estimate X1 = G, W = P, X2 = A. The host describes each
 // layer of a call once; a prepare kernel writes those descriptions, the work
-// item lists and the MFMA-packed W into the workspace, so one launch of each
-// stage covers every layer of a call.
+// item lists and (unless stage 1 reads W in place) the MFMA-packed W into the
+// workspace, so one launch of each stage covers every layer of a call. A call
+// over one layer whose W is read in place needs no prepare launch at all
+// (StageArgs' implicit mode).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -1,5 +1,6 @@
 // Kernels of the projected-contraction path on gfx950: the prepare pass
-// (layer records, work-item lists, MFMA-packed W), the skinny row projection
+// (layer records, work-item lists, MFMA-packed W where W is not read in
+// place), the skinny row projection
 // V = X1 W (stage 1), the T contraction Y = X2^T V with a fused squared
 // Frobenius reduction (stage 2), the split-T reduction, the per-sample
 // finisher and the clip factors.

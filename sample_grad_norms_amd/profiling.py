@@ -40,14 +40,24 @@ def source_files() -> List[str]:
                   if p.endswith((".hip", ".h", ".cpp")))
 
 
+_COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
+
+
+def code_text(src: str) -> str:
+    """C/HIP source without its comments and with whitespace runs collapsed:
+    what a summary's counters depend on (a comment edit leaves it valid)."""
+    return " ".join(_COMMENT.sub(" ", src).split())
+
+
 def source_hash(files: Optional[List[str]] = None) -> str:
-    """sha256 over the named csrc files (default: all of them). A file that
-    no longer exists hashes as missing, so the summary reads as stale."""
+    """sha256 over the code (comments and layout dropped) of the named csrc
+    files (default: all of them). A file that no longer exists hashes as
+    missing, so the summary reads as stale."""
     h = hashlib.sha256()
     for name in sorted(files if files is not None else source_files()):
         h.update(name.encode())
         path = os.path.join(HERE, "csrc", name)
-        h.update(open(path, "rb").read() if os.path.exists(path) else b"<missing>")
+        h.update(code_text(open(path, encoding="utf-8").read()).encode() if os.path.exists(path) else b"<missing>")
     return h.hexdigest()
 
 

@@ -62,6 +62,8 @@ def test_staleness_follows_only_the_named_sources(tmp_path, monkeypatch):
     assert profiling.read_traffic(out, "k_rowproj") is not None
     (csrc / "b.hip").write_text("kernel b v2")            # another kernel's source: still valid
     assert profiling.read_traffic(out, "k_rowproj") is not None
+    (csrc / "a.hip").write_text("kernel a v1  // a comment\n/* and\n another */")   # comments only: still valid
+    assert profiling.read_traffic(out, "k_rowproj") is not None
     (csrc / "a.hip").write_text("kernel a v2")            # the profiled kernel changed: stale
     assert profiling.read_traffic(out, "k_rowproj") is None
     # without a source list the hash covers every csrc file
@@ -70,6 +72,12 @@ def test_staleness_follows_only_the_named_sources(tmp_path, monkeypatch):
     assert profiling.read_traffic(out_all, "k_rowproj") is not None
     (csrc / "b.hip").write_text("kernel b v3")
     assert profiling.read_traffic(out_all, "k_rowproj") is None
+
+
+def test_code_text_drops_comments_and_layout():
+    src = "int a; // one\n/* two\n lines */ int  b;\n\tint c;"
+    assert profiling.code_text(src) == "int a; int b; int c;"
+    assert profiling.code_text('asm("s_nop 0\\n\\tx");') == 'asm("s_nop 0\\n\\tx");'
 
 
 def test_missing_calibration_copy_is_an_error(tmp_path):
