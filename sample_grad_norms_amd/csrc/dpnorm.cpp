@@ -225,8 +225,8 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   }
 }
 
-int pass_launches(const PassPlan& pl, int nl) {
-  (void)nl;
+// Launches of a pass at most (a pass that reads W in place may skip its prepare).
+int pass_launches(const PassPlan& pl) {
   const int entries = (int)pl.entries.size();
   const int classes = (int)pl.class_ncb.size();
   return (entries + kPrepChunk - 1) / kPrepChunk + 1 + classes * (pl.needs_ysum() ? 2 : 1);
@@ -585,7 +585,7 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
   if (c && c != n && overlaps(c, nb, n, nb)) return DPNORM_ERR_VALUE;
   if (trace) {
     if (!trace->events || !trace->kinds) return DPNORM_ERR_NULL;
-    const int need = pass_launches(hc.plan, (int)L) + 1;
+    const int need = pass_launches(hc.plan) + 1;
     if (trace->capacity < need + 1) return DPNORM_ERR_SIZE;
   }
 
