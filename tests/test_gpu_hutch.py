@@ -132,7 +132,7 @@ def test_deterministic_bitwise():
 
 
 @pytest.mark.parametrize("B,T,d,p,k", [(3, 333, 1032, 520, 32), (32, 1000, 264, 136, 32), (4, 200, 136, 64, 64),
-                                       (2, 128, 2048, 512, 16)])
+                                       (2, 128, 2048, 512, 16), (2, 300, 40, 24, 32), (5, 64, 16, 8, 16)])
 def test_projection_read_in_place_matches_packed_copy(B, T, d, p, k):
     """A single-layer bf16 call whose P is 16-byte aligned with k = 16, 32 or
     64 reads P in place; the same values 2 bytes further on take the packed
