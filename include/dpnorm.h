@@ -220,7 +220,7 @@ dpnorm_status dpnorm_norms_routed(const dpnorm_layer* layers, int64_t L, dpnorm_
  *   X = O S with O = G^T A A^T G, formed as G^T (A (A^T (G S)));
  *   Q = orthonormal basis of Col(X) by Gram-Schmidt in fp64, each column
  *       projected against the kept columns twice; column j of X is kept
- *       when its residual exceeds 1e-5 times the largest column norm of X
+ *       when its residual exceeds 1e-4 times the largest column norm of X
  *       (rank r_i <= m_s);
  *   head = ||A^T (G Q)||_F^2, tail = ||A^T (G (P - Q Q^T P))||_F^2,
  *   n_hat = head + tail.

@@ -40,7 +40,7 @@ from typing import Iterable, Sequence, Tuple
 
 import numpy as np
 
-RANK_TAU = 1e-5
+RANK_TAU = 1e-4   # well above the rounding an fp32 sketch of bf16 data carries (about 1e-5 of its norm)
 
 
 def to_f64(x) -> np.ndarray:

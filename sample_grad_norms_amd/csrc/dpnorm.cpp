@@ -606,7 +606,8 @@ dpnorm_status hutch_impl(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
 // ---------------------------------------------------------------------------
 // Hutch++ (three passes, basis and tail in between)
 // ---------------------------------------------------------------------------
-constexpr float kRankTau = 1e-5f;  // column kept when residual > tau * largest sketch column norm
+constexpr float kRankTau = 1e-4f;  // column kept when residual > tau * largest sketch column norm (the sketch's
+                                    // own rounding, about 1e-5 of it, stays well below)
 constexpr int kMaxSketch = 32;      // sketch columns handled by the basis kernel
 
 struct HppCall {

@@ -25,7 +25,7 @@
 // Columns keep their positions: a dropped column of X gives a zero column of
 // Q, which adds nothing to the head. W3 = [Q (MP columns) | P' (m_t)].
 // The rank rule bounds the condition number of the kept columns by about
-// 1/tau, so Q is orthonormal to about (1/tau)^2 * 2^-53 ~ 1e-6 in fp64.
+// 1/tau, so Q is orthonormal to about (1/tau)^2 * 2^-53 ~ 1e-8 in fp64.
 #include <cstring>
 
 #include "device_common.h"
