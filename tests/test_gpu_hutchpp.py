@@ -1,9 +1,10 @@
 """GPU parity of Hutch++ against the fp64 CPU oracle (same A, G, S, P).
 
-The estimate, its exact head ||A^T G Q||^2, its Hutchinson tail
-||A^T G (I - QQ^T) P||^2 and the kept rank must match the oracle ('Efficient
-DP-SGD for LLMs with Randomized Clipping', papernotes.org note, 关键设计 ›
-Hutch++), within 1e-3 relative for bf16 inputs and 1e-5 for fp32.
+The estimate must match the oracle ('Efficient DP-SGD for LLMs with
+Randomized Clipping', papernotes.org note, 关键设计 › Hutch++) within 1e-3
+relative for bf16 inputs and 1e-5 for fp32; its exact head ||A^T G Q||^2 and
+Hutchinson tail ||A^T G (I - QQ^T) P||^2 within the same fraction of the
+estimate, and the kept rank exactly.
 """
 import math
 
@@ -31,8 +32,14 @@ def run(prob_A, prob_G, S, P, tol, what):
     n, head, tail, rank = dp.hutchpp(prob_A, prob_G, S, P, return_parts=True)
     torch.cuda.synchronize()
     wn, wh, wt, wr = oracle.hutchpp(prob_A, prob_G, S, P)
-    en, eh, et = rel(n.cpu(), wn), rel(head.cpu(), wh), rel(tail.cpu(), wt)
-    print(f"{what}: n {en.max():.2e} head {eh.max():.2e} tail {et.max():.2e} rank {rank.cpu().tolist()} "
+    # the estimate to the tolerance; head and tail, its two parts, to the same
+    # tolerance of the estimate (a tail that is only rounding when the sketch
+    # spans all of O has no relative accuracy of its own)
+    en = rel(n.cpu(), wn)
+    scale = np.maximum(np.abs(np.asarray(wn, np.float64)), 1e-300)
+    eh = np.abs(head.cpu().double().numpy() - wh) / scale
+    et = np.abs(tail.cpu().double().numpy() - wt) / scale
+    print(f"{what}: n {en.max():.2e} head {eh.max():.2e} tail {et.max():.2e} (of n) rank {rank.cpu().tolist()} "
           f"oracle rank {wr.tolist()}", flush=True)
     assert np.array_equal(rank.cpu().numpy(), wr)
     assert np.all(en <= tol) and np.all(eh <= tol) and np.all(et <= tol)
@@ -41,7 +48,10 @@ def run(prob_A, prob_G, S, P, tol, what):
 
 @pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 1e-3), (torch.float32, 1e-5)])
 @pytest.mark.parametrize("B,T,d,p,k", [(2, 300, 264, 136, 32), (3, 77, 64, 520, 3), (1, 1000, 1032, 64, 96),
-                                       (2, 129, 8, 16, 12)])
+                                       (2, 129, 8, 16, 12),
+                                       # sketches of lower rank than m_s (T = 2; d = 16 < m_s = 32): the
+                                       # dependent columns' residuals are rounding, far below the threshold
+                                       (7, 2, 1000, 480, 32), (3, 1500, 16, 88, 96)])
 def test_hutchpp_shapes(dtype, tol, B, T, d, p, k):
     ms, mt = oracle.hutchpp_split(k)
     pr = workloads.random_problem(B, T, d, p, k, seed=T + d + k, device=dev(), dtype=dtype)
