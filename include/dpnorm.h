@@ -218,10 +218,12 @@ dpnorm_status dpnorm_norms_routed(const dpnorm_layer* layers, int64_t L, dpnorm_
  * suggested) and P is [p][m_t] (tail, entries of variance 1/m_t), both shared
  * by the samples. Per sample:
  *   X = O S with O = G^T A A^T G, formed as G^T (A (A^T (G S)));
- *   Q = orthonormal basis of Col(X) by Gram-Schmidt in fp64, each column
- *       projected against the kept columns twice; column j of X is kept
- *       when its residual exceeds 1e-4 times the largest column norm of X
- *       (rank r_i <= m_s);
+ *   Q = orthonormal basis of Col(X) (X formed in fp32), the Q factor of a
+ *       Cholesky QR in fp64 with positive diagonal; column j of X is kept
+ *       when its residual after projecting out the kept columns before it
+ *       (the Cholesky diagonal) exceeds 1e-4 times the largest column norm
+ *       of X (rank r_i <= m_s; when O has lower rank than m_s, columns past
+ *       it hold only rounding and may still be counted);
  *   head = ||A^T (G Q)||_F^2, tail = ||A^T (G (P - Q Q^T P))||_F^2,
  *   n_hat = head + tail.
  * n (+)= n_hat as for dpnorm_hutch. head, tail (float [B]) and rank (int32
