@@ -175,6 +175,30 @@ def test_grouped_projection_read_in_place_matches_packed_copy():
     check(a.cpu(), want, 1e-3, "grouped, P in place")
 
 
+def test_launch_sequence_follows_the_projection_layout():
+    """The traced launches: a one-layer call whose P is read in place has no
+    prepare launch; the same P 2 bytes further on is packed first (one
+    prepare); a two-layer call reads both P in place but its prepare still
+    writes the records and item lists."""
+    import sample_grad_norms_amd as dp
+    pr = workloads.random_problem(2, 1000, 264, 520, 32, seed=61, device=dev(), dtype=torch.bfloat16)
+    pr2 = workloads.random_problem(2, 1000, 136, 64, 32, seed=62, device=dev(), dtype=torch.bfloat16)
+    buf = torch.empty(pr.P.numel() + 8, dtype=torch.bfloat16, device=dev())
+    buf[1:1 + pr.P.numel()].copy_(pr.P.reshape(-1))
+    shifted = buf[1:1 + pr.P.numel()].view(pr.P.shape)
+    kinds = []
+    for layers in ([(pr.A, pr.G, pr.P)], [(pr.A, pr.G, shifted)], [(pr.A, pr.G, pr.P), (pr2.A, pr2.G, pr2.P)]):
+        timer = dp.KernelTimer()
+        dp.hutch_grouped(layers, timer=timer)
+        kinds.append([name for name, _ in timer.last()])
+    print(kinds, flush=True)
+    assert "prepare" not in kinds[0] and kinds[0][0] == "rowproj"
+    assert kinds[1].count("prepare") == 1 and kinds[1][0] == "prepare"
+    assert kinds[2].count("prepare") == 1
+    for ks in kinds:
+        assert ks[-1] == "finish" and ks.count("rowproj") == 1
+
+
 def test_clip_factor_kernel_special_values():
     import sample_grad_norms_amd as dp
     n = torch.tensor([0.0, float("inf"), float("nan"), 4.0, 16.0, 1.0, 64.0, 1e-30], device=dev())
