@@ -1,5 +1,5 @@
-"""Runs one named single-layer workload a few times, for profiling with
-rocprofv3 (the 112-projection stack is profiled through bench.py).
+"""Runs one named workload a few times, for profiling with rocprofv3 (the
+112-projection stack with independent inputs is profiled through bench.py).
 
     python sample_grad_norms_amd/profile_workloads.py NAME [--reps R] [--calib-copy]
 
@@ -9,6 +9,10 @@ NAME is one of:
   hutchpp             Hutch++, B=4, T=4096, d=p=2048, budget 32
   single_layer        Hutchinson, B=8, T=1024, d=p=2048, k=32
   single_layer_gram   the exact Gram route on the same inputs
+  shared_stack        the Llama-3.2-1B-shaped stack with q/k/v and gate/up
+                      sharing their input (grouped Hutchinson, B=4, T=4096, k=32)
+  sign_stack          the stack with +-1 projections stored as bits
+  lora_routed         rank-16 LoRA factors of the stack, routed call (exact norms)
 --calib-copy first runs one 1 GiB device-to-device copy, the reference the
 counter summaries scale FETCH_SIZE and WRITE_SIZE by.
 """
@@ -22,7 +26,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-NAMES = ("long_context_hutch", "long_context_exact", "hutchpp", "single_layer", "single_layer_gram")
+NAMES = ("long_context_hutch", "long_context_exact", "hutchpp", "single_layer", "single_layer_gram", "shared_stack",
+         "sign_stack", "lora_routed")
 
 
 def main() -> None:
@@ -46,6 +51,18 @@ def main() -> None:
     elif a.name == "hutchpp":
         pr = workloads.config4(device=dev)
         fn = lambda: dp.hutchpp(pr.A, pr.G, pr.S, pr.P, k=pr.k)
+    elif a.name == "shared_stack":
+        layers = workloads.shared_input_stack(device=dev)
+        fn = lambda: dp.hutch_grouped(layers, C_clip=1.0)
+    elif a.name == "sign_stack":
+        projs = [workloads.config3_projection(j, device=dev) for j in range(112)]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2024)
+        triples = [(q.A, q.G, dp.random_signs(q.G.shape[2], 32, device=dev, generator=gen)) for q in projs]
+        fn = lambda: dp.hutch_sign_grouped(triples, 32, C_clip=1.0)
+    elif a.name == "lora_routed":
+        routed = [(A, G, None) for (A, G, _) in workloads.lora_stack(device=dev)]
+        fn = lambda: dp.norms_routed(routed, 32)
     else:
         pr = workloads.config2(device=dev)
         fn = (lambda: dp.exact(pr.A, pr.G, route="gram")) if a.name.endswith("gram") else (lambda: dp.hutch(pr.A, pr.G, pr.P))
