@@ -13,6 +13,9 @@ NAME is one of:
                       sharing their input (grouped Hutchinson, B=4, T=4096, k=32)
   sign_stack          the stack with +-1 projections stored as bits
   lora_routed         rank-16 LoRA factors of the stack, routed call (exact norms)
+  dpsgd_step          DP-SGD-RC training steps on a random-init Llama-width stack
+                      (2 decoder layers, B=4, T=2048, bf16): forward, backward 1,
+                      the norm path, backward 2 of sum c_i l_i, noise, Adam
 --calib-copy first runs one 1 GiB device-to-device copy, the reference the
 counter summaries scale FETCH_SIZE and WRITE_SIZE by.
 """
@@ -27,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 NAMES = ("long_context_hutch", "long_context_exact", "hutchpp", "single_layer", "single_layer_gram", "shared_stack",
-         "sign_stack", "lora_routed")
+         "sign_stack", "lora_routed", "dpsgd_step")
 
 
 def main() -> None:
@@ -63,6 +66,23 @@ def main() -> None:
     elif a.name == "lora_routed":
         routed = [(A, G, None) for (A, G, _) in workloads.lora_stack(device=dev)]
         fn = lambda: dp.norms_routed(routed, 32)
+    elif a.name == "dpsgd_step":
+        from sample_grad_norms_amd.dpsgd_rc import RandomizedClipping
+        from workloads import llama_block as lb
+        shape = dict(layers=2, dim=2048, heads=32, kv_heads=8, hidden=8192, vocab=2048)
+        model = lb.build(90, device=dev, dtype=torch.bfloat16, **shape)
+        x, y = lb.batch(91, 4, 2048, shape["dim"], shape["vocab"], device=dev, dtype=torch.bfloat16)
+        rc = RandomizedClipping(model, C=1.0, noise_multiplier=1.0, k=32)
+        opt = torch.optim.Adam(rc.params, lr=1e-5)
+
+        def fn():
+            with rc.capture():
+                losses = lb.per_sample_loss(model(x), y)
+            n, c = rc.clip_factors(losses)
+            rc.clipped_backward(losses, c)
+            rc.add_noise()
+            opt.step()
+            opt.zero_grad(set_to_none=True)
     else:
         pr = workloads.config2(device=dev)
         fn = (lambda: dp.exact(pr.A, pr.G, route="gram")) if a.name.endswith("gram") else (lambda: dp.hutch(pr.A, pr.G, pr.P))

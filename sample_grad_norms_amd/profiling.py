@@ -120,7 +120,8 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str, out: str, cmds: Li
     lines = [f"# {title}", "", "Commands (run from the repository root on the GPU box):", ""]
     lines += ["```", *cmds, "```", "", "## Kernel statistics (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
-    for r in stats[:12]:
+    shown = stats[:12] + [r for r in stats[12:] if r["name"].startswith("k_")]   # the library's kernels always
+    for r in shown:
         lines.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.1f} | {r['total_ms']:.2f} | {r['pct']:.1f} |")
     lines += ["", f"## HBM traffic per dispatch (FETCH_SIZE x {ffac:.3f}, WRITE_SIZE x {wfac:.3f}; "
               "scales from a 1 GiB device-to-device copy)", "", "| kernel | read GB | written GB |", "|---|---|---|"]
