@@ -49,6 +49,22 @@ def test_basis_orthonormal_and_spanning():
     assert np.linalg.norm(X - Q @ (Q.T @ X)) <= 1e-12 * np.linalg.norm(X)
 
 
+def test_rank_threshold_is_relative_to_the_largest_column():
+    """A column is kept iff its residual after the kept columns before it
+    exceeds RANK_TAU times the largest column norm: residuals of 1.5 tau and
+    tau / 6 of that norm fall on either side of the rule, at any overall
+    scale."""
+    tau = oracle.RANK_TAU
+    for scale in (1e-3, 1.0, 1e5):
+        e = np.eye(6)
+        X = scale * np.stack([e[0], e[0] + 3 * tau * e[1], e[0] + tau / 3 * e[2], 2 * e[3], e[1]], axis=1)
+        # largest column norm is 2 scale; residuals: 1 (e0), 3 tau, tau / 3, 2, then 0 after e0 and e1
+        Q = oracle.orthonormal_basis(X)
+        assert Q.shape[1] == 3, scale
+        kept = np.abs(Q.T @ np.eye(6)) > 0.5
+        assert kept[:, 0].any() and kept[:, 1].any() and kept[:, 3].any() and not kept[:, 2].any()
+
+
 def test_basis_rank_deficient():
     rng = np.random.default_rng(22)
     X = rng.standard_normal((30, 3)) @ rng.standard_normal((3, 8))
