@@ -291,17 +291,24 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
 // Record 0 and both work lists, as the prepare kernel writes them for a lone
 // layer: items1 (0, sample, row block, 0), items2 (0, sample, column block,
 // T split) with the split innermost.
+// Every work group of the grid writes its own slice of the entries (work
+// group 0 also the record), so no group carries all of them.
 __device__ void hpp_write_tables(const HppNext& nx) {
-  for (int r = threadIdx.x; r < nx.n1; r += blockDim.x) {
-    const int i = r / nx.rbs;
-    nx.items1[r] = make_int4(0, i, r - i * nx.rbs, 0);
+  const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int total = nx.n1 + nx.n2, per = (total + nb - 1) / nb;
+  const int end = min(total, (b + 1) * per);
+  for (int r = b * per + threadIdx.x; r < end; r += blockDim.x) {
+    if (r < nx.n1) {
+      const int i = r / nx.rbs;
+      nx.items1[r] = make_int4(0, i, r - i * nx.rbs, 0);
+    } else {
+      const int r2 = r - nx.n1;
+      const int ts = r2 % nx.nsplit, q = r2 / nx.nsplit;
+      const int ub = q % nx.ubs, i = q / nx.ubs;
+      nx.items2[r2] = make_int4(0, i, ub, ts);
+    }
   }
-  for (int r = threadIdx.x; r < nx.n2; r += blockDim.x) {
-    const int ts = r % nx.nsplit, q = r / nx.nsplit;
-    const int ub = q % nx.ubs, i = q / nx.ubs;
-    nx.items2[r] = make_int4(0, i, ub, ts);
-  }
-  if (threadIdx.x == 0) nx.recs[0] = nx.rec;
+  if (b == 0 && threadIdx.x == 0) nx.recs[0] = nx.rec;
 }
 
 // The packed units of rows r0 .. r0 + 63 (r0 a multiple of 64) of sample
@@ -356,7 +363,7 @@ __global__ void __launch_bounds__(256) k_hpp_ysum_pack(const float* __restrict__
   }
   __syncthreads();
   hpp_pack_tile(tile, NC, r0, i, nx);
-  if (blockIdx.x == 0 && blockIdx.y == 0) hpp_write_tables(nx);
+  hpp_write_tables(nx);
 }
 
 // Q = X Ri and P' = P - X N for kApplyRows rows (16 per wave); K slot l / 16
@@ -433,7 +440,7 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
   if (pack) {  // uniform
     __syncthreads();
     hpp_pack_tile(tile, ldw, blockIdx.x * kApplyRows, i, nx);
-    if (blockIdx.x == 0 && blockIdx.y == 0) hpp_write_tables(nx);
+    hpp_write_tables(nx);
   }
 }
 
