@@ -105,3 +105,22 @@ def test_grouped_entry_points(case):
     print(f"{what}: grouped {e_g:.1e} clip {e_c:.1e} sign {e_s:.1e} routed {e_r:.1e} routes {list(routes)}", flush=True)
     assert e_g <= tol and e_c <= 1e-5 and e_s <= tol and e_r <= tol
     assert [int(x) for x in routes] == [int(x) for x in wroutes]
+
+
+@pytest.mark.parametrize("B,T,d,p,k", [(1, 131072, 1024, 1024, 32), (256, 1, 2048, 512, 32), (64, 513, 264, 1032, 32),
+                                       (2, 65536, 8, 8192, 64)])
+def test_extreme_shapes(B, T, d, p, k):
+    """Long sequences (T = 2^17 and 2^16 with the narrowest d), a large batch
+    of single tokens and a 64-sample batch: Hutchinson and Hutch++ against
+    the oracle, bf16."""
+    import sample_grad_norms_amd as dp
+    pr = workloads.random_problem(B, T, d, p, k, seed=B + T, device=dev(), dtype=torch.bfloat16)
+    ms, mt = oracle.hutchpp_split(k)
+    S = workloads.gaussian((p, ms), 1.0, 5, dev(), torch.bfloat16)
+    Pt = workloads.projection(p, mt, 6, dev(), torch.bfloat16)
+    n = dp.hutch(pr.A, pr.G, pr.P)
+    nh = dp.hutchpp(pr.A, pr.G, S, Pt)
+    torch.cuda.synchronize()
+    e, eh = rel(n.cpu(), oracle.hutch(pr.A, pr.G, pr.P)), rel(nh.cpu(), oracle.hutchpp(pr.A, pr.G, S, Pt)[0])
+    print(f"B{B} T{T} d{d} p{p} k{k}: hutch {e:.1e} hutch++ {eh:.1e}", flush=True)
+    assert e <= 1e-3 and eh <= 1e-3
