@@ -33,6 +33,57 @@ def test_hand_example():
     assert t2[0] == 1.0 and n2[0] == c["n_exact"]
 
 
+def _golden(name):
+    with open(GOLDEN) as f:
+        return {x["name"]: x for x in json.load(f)["cases"]}[name]
+
+
+def _frac(x):
+    return x[0] / x[1]
+
+
+@pytest.mark.parametrize("name", ["hutchpp_sketch_direction", "hutchpp_sketch_rectangular"])
+def test_hand_examples_where_the_sketch_direction_depends_on_O(name):
+    """S is not an eigenvector of O, so the basis direction, and with it the
+    head, depends on every factor of O S = G^T A A^T G S: a sketch that drops
+    A A^T, works in d-space or transposes G gives another head (the hand
+    derivations list them)."""
+    c = _golden(name)
+    A, G = np.array([c["A"]], float), np.array([c["G"]], float)
+    S, P = np.array(c["S"], float), np.array(c["P"], float)
+    X = oracle.hutchpp_sketch(A[0], G[0], S)
+    np.testing.assert_allclose(X, np.array(c["sketch"], float), rtol=0, atol=1e-12)
+    n, head, tail, rank = oracle.hutchpp(A, G, S, P)
+    assert math.isclose(head[0], _frac(c["head"]), rel_tol=1e-12)
+    assert math.isclose(tail[0], _frac(c["tail"]), rel_tol=1e-12, abs_tol=1e-12)
+    assert math.isclose(n[0], _frac(c["n_hutchpp"]), rel_tol=1e-12)
+    assert rank[0] == 1
+    assert oracle.exact_explicit(A, G)[0] == c["n_exact"]
+
+
+def test_sketch_equals_O_times_S_with_O_built_entrywise():
+    """X = O S with O[u][v] = sum_{t,s} G[t,u] (a_t . a_s) G[s,v], summed
+    entry by entry in pure Python (T x T token similarities, no matrix
+    product), on non-square inputs with p != d."""
+    rng = np.random.default_rng(31)
+    T, d, p, m = 5, 3, 4, 2
+    A = rng.standard_normal((T, d))
+    G = rng.standard_normal((T, p))
+    S = rng.standard_normal((p, m))
+    K = [[sum(A[t, u] * A[s, u] for u in range(d)) for s in range(T)] for t in range(T)]
+    O = [[sum(G[t, u] * K[t][s] * G[s, v] for t in range(T) for s in range(T)) for v in range(p)]
+         for u in range(p)]
+    want = np.array([[sum(O[u][v] * S[v, j] for v in range(p)) for j in range(m)] for u in range(p)])
+    got = oracle.hutchpp_sketch(A, G, S)
+    assert got.shape == (p, m)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # the head on the basis of that sketch is trace(Q^T O Q) with the same O
+    Q = oracle.orthonormal_basis(got)
+    head, _ = oracle.hutchpp_head_tail(A, G, Q, np.zeros((p, 1)))
+    O = np.array(O)
+    assert math.isclose(head, float(np.trace(Q.T @ O @ Q)), rel_tol=1e-12)
+
+
 def test_budget_split():
     assert oracle.hutchpp_split(32) == (11, 10)
     assert oracle.hutchpp_split(96) == (32, 32)
