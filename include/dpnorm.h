@@ -226,13 +226,24 @@ dpnorm_status dpnorm_norms_routed(const dpnorm_layer* layers, int64_t L, dpnorm_
  *       it hold only rounding and may still be counted);
  *   head = ||A^T (G Q)||_F^2, tail = ||A^T (G (P - Q Q^T P))||_F^2,
  *   n_hat = head + tail.
- * n (+)= n_hat as for dpnorm_hutch. head, tail (float [B]) and rank (int32
- * [B]) are optional outputs (NULL to skip); they hold this call's values.
+ * n (+)= n_hat as for dpnorm_hutch. head, tail (float [B]), rank (int32
+ * [B]) and resid (float [B][m_s]) are optional outputs (NULL to skip); they
+ * hold this call's values. resid[i][j] is the residual that decided column j
+ * of sample i (the Cholesky pivot's square root) over the largest column
+ * norm of X_i, so column j is kept iff resid[i][j] > 1e-4 (0 for a zero
+ * sketch). The rank is an integer decided on rounded floating point: when
+ * O_i has full rank on the sketch (every resid well above 1e-4) it is m_s and
+ * matches an exact computation; when O_i has rank below m_s (T, d or p below
+ * m_s, or G_i or A_i of low rank) the residuals past that rank hold only the
+ * rounding of the fp32 sketch, which can land on either side of 1e-4, so
+ * rank may then count some of those columns (the estimate is unaffected:
+ * such columns carry rounding-sized parts of O between head and tail).
+ * Outputs must not overlap each other, the inputs or ws.
  * k is the total budget, 3 <= k <= 96 (so m_s <= 32 and m_s + m_t <= 64). */
 dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const void* P, dpnorm_dtype dt,
                              int64_t B, int64_t T, int64_t d, int64_t p, int64_t k, float* n,
-                             int accumulate, float* head, float* tail, int32_t* rank, void* ws,
-                             size_t ws_bytes, hipStream_t stream);
+                             int accumulate, float* head, float* tail, int32_t* rank, float* resid,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Exact squared per-sample norm n_i = ||A_i^T G_i||_F^2 (the comparator:
  * note 研究背景与动机 and 相关工作, explicit gradients vs ghost clipping;

@@ -5,6 +5,7 @@ and the ``cpu_baseline`` leg of ``bench.py``; never by the product package.
 """
 from .reference import (  # noqa: F401
     RANK_TAU,
+    basis_residuals,
     clip_factors,
     exact_explicit,
     exact_gram,

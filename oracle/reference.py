@@ -185,26 +185,43 @@ def hutchpp_split(k: int) -> Tuple[int, int]:
     return m_s, int(k) - 2 * m_s
 
 
-def orthonormal_basis(X, tau: float = RANK_TAU) -> np.ndarray:
-    """Orthonormal basis of the column span of X (p x m) by sequential
-    Gram-Schmidt, each column projected against the kept basis twice.
-    A column is kept iff its residual norm exceeds tau * max_j ||x_j||.
-    Returns Q (p x r), r <= m."""
+def _gram_schmidt(X, tau: float):
+    """Sequential Gram-Schmidt over the columns of X (p x m), each column
+    projected against the kept basis twice; column j is kept iff its residual
+    norm exceeds tau * max_a ||x_a||. Returns the kept unit vectors and, per
+    column, that residual norm over max_a ||x_a|| (0 for a zero X)."""
     X = to_f64(X)
     p, m = X.shape
     scale = max((np.linalg.norm(X[:, j]) for j in range(m)), default=0.0)
-    basis = []
+    basis, resid = [], []
     for j in range(m):
         v = X[:, j].copy()
         for _ in range(2):
             for q in basis:
                 v -= q * np.dot(q, v)
         nv = np.linalg.norm(v)
+        resid.append(nv / scale if scale > 0.0 else 0.0)
         if nv > tau * scale and nv > 0.0:
             basis.append(v / nv)
+    return basis, np.array(resid)
+
+
+def orthonormal_basis(X, tau: float = RANK_TAU) -> np.ndarray:
+    """Orthonormal basis of the column span of X (p x m) by sequential
+    Gram-Schmidt, each column projected against the kept basis twice.
+    A column is kept iff its residual norm exceeds tau * max_j ||x_j||.
+    Returns Q (p x r), r <= m."""
+    basis, _ = _gram_schmidt(X, tau)
     if not basis:
-        return np.zeros((p, 0))
+        return np.zeros((to_f64(X).shape[0], 0))
     return np.stack(basis, axis=1)
+
+
+def basis_residuals(X, tau: float = RANK_TAU) -> np.ndarray:
+    """Per column of X, the residual norm that the rank rule of
+    orthonormal_basis compares with tau (relative to the largest column
+    norm): column j is kept iff this value exceeds tau."""
+    return _gram_schmidt(X, tau)[1]
 
 
 def hutchpp_sample(A_i, G_i, S, P, tau: float = RANK_TAU):

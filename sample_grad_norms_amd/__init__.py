@@ -370,12 +370,14 @@ def exact_workspace(dtype: torch.dtype, B: int, T: int, d: int, p: int, route: s
 
 def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, k: Optional[int] = None,
             out: Optional[torch.Tensor] = None, accumulate: bool = False, return_parts: bool = False,
-            workspace: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, return_residuals: bool = False):
     """Hutch++ estimate with total budget k (dpnorm_hutchpp).
 
     S [p][m_s] is the sketch and P [p][m_t] the tail projection, with
     (m_s, m_t) = hutchpp_split(k); by default k = 2 m_s + m_t from the
-    shapes. Returns n [B], or (n, head, tail, rank) with return_parts.
+    shapes. Returns n [B], or (n, head, tail, rank) with return_parts;
+    return_residuals appends resid [B][m_s], the relative residual of each
+    sketch column that the rank rule compared with its threshold.
     ``workspace`` (uint8, GPU) may be passed to reuse one allocation.
     """
     _need(A, "A", 3)
@@ -399,12 +401,16 @@ def hutchpp(A: torch.Tensor, G: torch.Tensor, S: torch.Tensor, P: torch.Tensor, 
     head = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
     tail = torch.empty(B, dtype=torch.float32, device=device) if return_parts else None
     rank = torch.empty(B, dtype=torch.int32, device=device) if return_parts else None
+    resid = torch.empty(B, ms, dtype=torch.float32, device=device) if return_residuals else None
     ws, wsp = _given_workspace(workspace, nbytes.value, device)
     ptr = lambda t: t.data_ptr() if t is not None else None
     _check(L.dpnorm_hutchpp(A.data_ptr(), G.data_ptr(), S.data_ptr(), P.data_ptr(), _code(dtype), B, T, d, p, k,
-                            n.data_ptr(), int(accumulate), ptr(head), ptr(tail), ptr(rank), wsp, nbytes.value,
-                            _stream(device)), "dpnorm_hutchpp")
-    return (n, head, tail, rank) if return_parts else n
+                            n.data_ptr(), int(accumulate), ptr(head), ptr(tail), ptr(rank), ptr(resid), wsp,
+                            nbytes.value, _stream(device)), "dpnorm_hutchpp")
+    out_ = (n, head, tail, rank) if return_parts else (n,)
+    if return_residuals:
+        out_ = out_ + (resid,)
+    return out_ if len(out_) > 1 else n
 
 
 def exact(A: torch.Tensor, G: torch.Tensor, route: str = "auto", out: Optional[torch.Tensor] = None,

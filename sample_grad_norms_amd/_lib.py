@@ -60,7 +60,7 @@ SIGNATURES = {
                                      _sz, _vp, C.POINTER(Trace)], C.c_int),
     "dpnorm_hutchpp_workspace": ([C.c_int, _i64, _i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "dpnorm_hutchpp": ([_vp, _vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _vp, _vp, _vp,
-                        _sz, _vp], C.c_int),
+                        _vp, _sz, _vp], C.c_int),
     "dpnorm_exact_workspace": ([C.c_int, _i64, _i64, _i64, _i64, C.c_int, C.POINTER(_sz)], C.c_int),
     "dpnorm_exact": ([_vp, _vp, C.c_int, _i64, _i64, _i64, _i64, C.c_int, _vp, C.c_int, _vp, _sz, _vp], C.c_int),
     "dpnorm_clip_factors": ([_vp, _i64, _f32, _vp, _vp], C.c_int),

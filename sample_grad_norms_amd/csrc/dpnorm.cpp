@@ -825,13 +825,15 @@ dpnorm_status dpnorm_hutchpp_workspace(dpnorm_dtype dt, int64_t B, int64_t T, in
 
 dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const void* P, dpnorm_dtype dt, int64_t B,
                              int64_t T, int64_t d, int64_t p, int64_t k, float* n, int accumulate, float* head,
-                             float* tail, int32_t* rank, void* ws, size_t ws_bytes, hipStream_t stream) {
+                             float* tail, int32_t* rank, float* resid, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   HppCall hc;
   dpnorm_status st = build_hutchpp(A, G, S, P, dt, B, T, d, p, k, true, hc);
   if (st != DPNORM_OK) return st;
   if (!n) return DPNORM_ERR_NULL;
   if (accumulate != 0 && accumulate != 1) return DPNORM_ERR_VALUE;
-  if (!aligned(n, 4) || (head && !aligned(head, 4)) || (tail && !aligned(tail, 4)) || (rank && !aligned(rank, 4)))
+  if (!aligned(n, 4) || (head && !aligned(head, 4)) || (tail && !aligned(tail, 4)) || (rank && !aligned(rank, 4)) ||
+      (resid && !aligned(resid, 4)))
     return DPNORM_ERR_ALIGN;
   if (!ws) return DPNORM_ERR_NULL;
   if (ws_bytes < hc.bytes) return DPNORM_ERR_WORKSPACE;
@@ -839,15 +841,16 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   const size_t nb = (size_t)B * 4, e = esize(dt);
   const size_t sa = (size_t)B * T * d * e, sg = (size_t)B * T * p * e;
   const size_t ss = (size_t)p * hc.ms * e, sp = (size_t)p * hc.mt * e;
-  const void* outs[4] = {n, head, tail, rank};
-  for (int j = 0; j < 4; ++j) {
+  const void* outs[5] = {n, head, tail, rank, resid};
+  const size_t ob[5] = {nb, nb, nb, nb, nb * (size_t)hc.ms};
+  for (int j = 0; j < 5; ++j) {
     const void* o = outs[j];
     if (!o) continue;
-    if (overlaps(o, nb, A, sa) || overlaps(o, nb, G, sg) || overlaps(o, nb, S, ss) || overlaps(o, nb, P, sp) ||
-        overlaps(o, nb, ws, hc.bytes))
+    if (overlaps(o, ob[j], A, sa) || overlaps(o, ob[j], G, sg) || overlaps(o, ob[j], S, ss) ||
+        overlaps(o, ob[j], P, sp) || overlaps(o, ob[j], ws, hc.bytes))
       return DPNORM_ERR_VALUE;
-    for (int q = j + 1; q < 4; ++q)
-      if (outs[q] && overlaps(o, nb, outs[q], nb)) return DPNORM_ERR_VALUE;
+    for (int q = j + 1; q < 5; ++q)
+      if (outs[q] && overlaps(o, ob[j], outs[q], ob[q])) return DPNORM_ERR_VALUE;
   }
   char* base = (char*)ws;
   hc.l1[0].Yout = (float*)(base + hc.off_ys);
@@ -870,7 +873,8 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr, !fuse2);
   if (he == hipSuccess)
     he = launch_hpp_qr((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.mt, P,
-                       dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, base + hc.off_qr,
+                       dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, resid, (int)hc.ms,
+                       base + hc.off_qr,
                        fuse3 ? &nx3 : nullptr, stream);
   if (he == hipSuccess) he = run_pass(hc.p3, hc.l3, base, stream, tr, !fuse3);
   if (he == hipSuccess)

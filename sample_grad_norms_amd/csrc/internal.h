@@ -141,7 +141,8 @@ struct HppNext {
 // next == nullptr: W3 is written; else next's packed W (from the same values) and
 // tables are written in its place, and W3 is not.
 hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, void* scratch, const HppNext* next, hipStream_t s);
+                         int ldw, int32_t* rank, float* resid, int ms, void* scratch, const HppNext* next,
+                         hipStream_t s);
 // The split-T sum of a stored pass, Ypart [nsplit][B][w][NC] fp32 summed in
 // split order (fp64), packed straight into `next`'s projection (the stored
 // Y of that pass is not written), with next's tables.

@@ -132,6 +132,7 @@ template <int MP>
 struct HppBasis {
   double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail], N[MP][kMaxTail];
   double sj[MP];   // 1 / R[j][j] of kept columns, 0 of dropped ones
+  double xmax2;    // the largest squared column norm of X
 };
 
 // Run by all 256 threads of a work group (it holds barriers): sum of sample
@@ -210,6 +211,7 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   for (int j = 0; j < MP; ++j) dmax = fmax(dmax, Sc[j][j]);
   const double thr = (double)tau * sqrt(fmax(dmax, 0.0));
   const double thr2 = thr * thr;
+  if (l == 0) sb.xmax2 = dmax;
   __syncthreads();
   uint32_t keep = 0;
   for (int j = 0; j < MP; ++j) {
@@ -374,7 +376,8 @@ template <int MP>
 __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, int p, int mt,
                                                    const void* __restrict__ P, int ptype,
                                                    const double* __restrict__ part, int nparts, float tau,
-                                                   int32_t* rank_out, float* W3, int ldw, int pack, HppNext nx) {
+                                                   int32_t* rank_out, float* resid_out, int ms, float* W3, int ldw,
+                                                   int pack, HppNext nx) {
   constexpr int TA = MP / 16;
   __shared__ HppBasis<MP> sb;
   __shared__ float tile[kApplyRows * (MP + kMaxTail)];   // this group's rows of W3, when packing
@@ -403,6 +406,14 @@ __global__ void __launch_bounds__(256) k_hpp_apply(const float* __restrict__ X, 
   }
   const uint32_t keep = hpp_basis<MP>(part, nparts, tau, i, sb);
   if (blockIdx.x == 0 && tid == 0 && rank_out) rank_out[i] = __popc(keep);
+  // the residual each keep decision compared with tau: the Cholesky pivot
+  // d_j (the squared residual of column j after the kept columns before it;
+  // the diagonal of the Schur complement keeps it) over the largest squared
+  // column norm, as a norm ratio
+  if (blockIdx.x == 0 && tid < ms && resid_out) {
+    const double m2 = sb.xmax2;
+    resid_out[(int64_t)i * ms + tid] = m2 > 0.0 ? (float)sqrt(fmax(sb.G[tid][tid], 0.0) / m2) : 0.f;
+  }
   double (&Ri)[MP][MP] = sb.Ri;
   double (&N)[MP][kMaxTail] = sb.N;
   __syncthreads();
@@ -453,7 +464,8 @@ size_t hpp_qr_scratch_bytes(int MP, int B, int p) {
 
 template <int MP>
 static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, char* scratch, const HppNext* next, hipStream_t s) {
+                         int ldw, int32_t* rank, float* resid, int ms, char* scratch, const HppNext* next,
+                         hipStream_t s) {
   const int nparts = (p + kGramRows - 1) / kGramRows;
   double* part = (double*)scratch;
   hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
@@ -463,15 +475,17 @@ static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, in
   std::memset(&nx, 0, sizeof(nx));
   if (next) nx = *next;
   hipLaunchKernelGGL(k_hpp_apply<MP>, dim3((p + kApplyRows - 1) / kApplyRows, B), dim3(256), 0, s, X, p, mt, P,
-                     ptype, (const double*)part, nparts, tau, rank, W3, ldw, next ? 1 : 0, nx);
+                     ptype, (const double*)part, nparts, tau, rank, resid, ms, W3, ldw, next ? 1 : 0, nx);
   return hipGetLastError();
 }
 
 hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, void* scratch, const HppNext* next, hipStream_t s) {
+                         int ldw, int32_t* rank, float* resid, int ms, void* scratch, const HppNext* next,
+                         hipStream_t s) {
   if (next && (ldw > MP + kMaxTail || next->ncols > ldw || next->NCB * 16 != ldw)) return hipErrorInvalidValue;
-  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, next, s);
-  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, (char*)scratch, next, s);
+  if (ms < 0 || ms > MP || ms > 256) return hipErrorInvalidValue;
+  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
+  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
   return hipErrorInvalidValue;
 }
 

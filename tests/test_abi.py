@@ -222,7 +222,7 @@ def test_hutchpp_checks(lib):
         assert lib.dpnorm_hutchpp_workspace(_lib.BF16, 2, 100, 64, 32, k, C.byref(nb)) == _lib.ERR_SIZE
     lib.dpnorm_hutchpp_workspace(_lib.BF16, 2, 100, 64, 32, 32, C.byref(nb))
     S_ADDR = 0x600000
-    args = [A_ADDR, G_ADDR, S_ADDR, P_ADDR, _lib.BF16, 2, 100, 64, 32, 32, N_ADDR, 0, None, None, None]
+    args = [A_ADDR, G_ADDR, S_ADDR, P_ADDR, _lib.BF16, 2, 100, 64, 32, 32, N_ADDR, 0, None, None, None, None]
     assert lib.dpnorm_hutchpp(*args, WS_ADDR, nb.value - 1, None) == _lib.ERR_WORKSPACE
     bad = list(args); bad[2] = None
     assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_NULL
@@ -232,6 +232,11 @@ def test_hutchpp_checks(lib):
     assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_DTYPE
     bad = list(args); bad[11] = 3
     assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_VALUE
+    # resid is [B][m_s] floats (2 x 11 at k = 32): one that reaches n overlaps it
+    bad = list(args); bad[15] = N_ADDR - 4 * 2 * 11 + 4
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_VALUE
+    bad = list(args); bad[15] = N_ADDR + 2
+    assert lib.dpnorm_hutchpp(*bad, WS_ADDR, nb.value, None) == _lib.ERR_ALIGN
 
 
 def test_exact_checks(lib):

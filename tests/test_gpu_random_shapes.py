@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import hutchpp_parity
 import oracle
 import workloads
 
@@ -49,27 +50,19 @@ def test_single_layer_estimators(case):
     ms, mt = oracle.hutchpp_split(kk)
     S = workloads.gaussian((p, ms), 1.0, 7200 + case, dev(), dt)
     Pt = workloads.projection(p, mt, 7300 + case, dev(), dt)
-    nh, head, tail, rank = dp.hutchpp(pr.A, pr.G, S, Pt, return_parts=True)
+    nh, head, tail, rank, resid = dp.hutchpp(pr.A, pr.G, S, Pt, return_parts=True, return_residuals=True)
     torch.cuda.synchronize()
     e_h = rel(n.cpu(), oracle.hutch(pr.A, pr.G, pr.P))
     e_x = rel(ne.cpu(), oracle.exact_explicit(pr.A, pr.G))
-    wn, wh, wt, wr = oracle.hutchpp(pr.A, pr.G, S, Pt)
-    e_pp = rel(nh.cpu(), wn)
-    scale = np.maximum(np.abs(wn), 1e-300)
-    e_parts = float(max((np.abs(head.cpu().double().numpy() - wh) / scale).max(),
-                        (np.abs(tail.cpu().double().numpy() - wt) / scale).max()))
-    print(f"{what}: hutch {e_h:.1e} exact/{route} {e_x:.1e} hutch++ k{kk} {e_pp:.1e} parts {e_parts:.1e} "
-          f"rank {rank.cpu().tolist()} oracle {wr.tolist()}", flush=True)
-    assert e_h <= tol and e_x <= tol and e_pp <= tol and e_parts <= tol
-    # the kept rank is decided on the kernel's sketch: where the sketch has
-    # full rank m_s it must match; where O has lower rank the columns past it
-    # hold only rounding, which the kernel's fp32 sketch (amplified by the
-    # conditioning of the kept columns) can lift above the threshold, so the
-    # rank may exceed the oracle's up to m_s while the estimate is unaffected
-    gr = rank.cpu().numpy()
-    full = wr == min(ms, p)
-    assert np.array_equal(gr[full], wr[full])
-    assert np.all(gr[~full] >= wr[~full]) and np.all(gr <= ms)
+    print(f"{what}: hutch {e_h:.1e} exact/{route} {e_x:.1e}", flush=True)
+    # Hutch++ by the shared rule: the kept rank is decided on the kernel's
+    # sketch; where the sketch has full rank m_s it must match the oracle's
+    # and head and tail are held to their own values; where O has lower rank
+    # the columns past it hold only rounding, so the rank may exceed the
+    # oracle's up to m_s while the estimate is unaffected
+    print(hutchpp_parity.check(pr.A, pr.G, S, (nh, head, tail, rank), oracle.hutchpp(pr.A, pr.G, S, Pt), tol,
+                               f"hutch++ k{kk}", resid=resid), flush=True)
+    assert e_h <= tol and e_x <= tol
 
 
 @pytest.mark.parametrize("case", range(8))

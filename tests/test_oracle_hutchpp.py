@@ -114,6 +114,11 @@ def test_rank_threshold_is_relative_to_the_largest_column():
         assert Q.shape[1] == 3, scale
         kept = np.abs(Q.T @ np.eye(6)) > 0.5
         assert kept[:, 0].any() and kept[:, 1].any() and kept[:, 3].any() and not kept[:, 2].any()
+        # the residuals the rule compared, relative to that largest norm
+        r = oracle.basis_residuals(X)
+        want = np.array([1.0, 3 * tau, tau / 3, 2.0, 0.0]) / 2.0
+        np.testing.assert_allclose(r, want, rtol=1e-6, atol=1e-15)
+    assert np.all(oracle.basis_residuals(np.zeros((4, 3))) == 0.0)
 
 
 def test_basis_rank_deficient():
