@@ -164,6 +164,28 @@ dpnorm_status dpnorm_hutch_grouped(const dpnorm_layer* layers, int64_t L, dpnorm
                                    int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dpnorm_hutch_grouped without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Scratch comes from a static device array
+ * of DPNORM_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; the call itself allocates and frees nothing.
+ * The caller still passes every input and output (n, and c when wanted).
+ * Arguments, semantics and errors as dpnorm_hutch_grouped, plus:
+ *   DPNORM_ERR_WORKSPACE when the call needs more scratch than
+ *     DPNORM_STATIC_SCRATCH_BYTES (the size dpnorm_hutch_grouped_workspace
+ *     reports for the same descriptors, or for NULL A pointers when sharing
+ *     A would not fit); checked before the device is touched;
+ *   DPNORM_ERR_VALUE when `stream` belongs to another device than the
+ *     current one.
+ * All calls on one GPU share its array, and it keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU, on different streams or host threads, race and must be serialised by
+ * the caller. */
+#define DPNORM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+dpnorm_status dpnorm_hutch_grouped_noalloc(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                           int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
+                                           hipStream_t stream);
+
 /* dpnorm_hutch_grouped with an event trace (see dpnorm_trace). */
 dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt,
                                           int64_t B, int64_t T, int64_t k, float* n, int accumulate,

@@ -13,6 +13,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdpnorm.so")
 
+# DPNORM_STATIC_SCRATCH_BYTES: the static scratch of dpnorm_hutch_grouped_noalloc
+STATIC_SCRATCH_BYTES = 64 << 20
 # dpnorm_status
 OK, ERR_NULL, ERR_SIZE, ERR_DTYPE, ERR_VALUE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(8)
 # dpnorm_dtype
@@ -56,6 +58,8 @@ SIGNATURES = {
     "dpnorm_hutch": ([_vp, _vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _i64, _vp, C.c_int, _vp, _sz, _vp], C.c_int),
     "dpnorm_hutch_grouped": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32, _vp, _sz,
                               _vp], C.c_int),
+    "dpnorm_hutch_grouped_noalloc": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32,
+                                      _vp], C.c_int),
     "dpnorm_hutch_grouped_traced": ([C.POINTER(Layer), _i64, C.c_int, _i64, _i64, _i64, _vp, C.c_int, _vp, _f32, _vp,
                                      _sz, _vp, C.POINTER(Trace)], C.c_int),
     "dpnorm_hutchpp_workspace": ([C.c_int, _i64, _i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),

@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -693,6 +694,44 @@ dpnorm_status exact_plan(dpnorm_dtype dt, int64_t B, int64_t T, int64_t d, int64
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (dpnorm_hutch_grouped_noalloc)
+// ---------------------------------------------------------------------------
+// One array per GPU, held from the module's load on that GPU until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is fetched once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DPNORM_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch array; the stream must
+// belong to that device.
+dpnorm_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DPNORM_ERR_HIP;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return DPNORM_ERR_HIP;
+    if (sd != dev) return DPNORM_ERR_VALUE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return DPNORM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DPNORM_OK;
+}
+
+}  // namespace
+
 // ===========================================================================
 // C ABI
 // ===========================================================================
@@ -777,6 +816,26 @@ dpnorm_status dpnorm_hutch_grouped_traced(const dpnorm_layer* layers, int64_t L,
                                           void* ws, size_t ws_bytes, hipStream_t stream, dpnorm_trace* trace) {
   if (!trace) return DPNORM_ERR_NULL;
   return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, ws_bytes, stream, trace);
+}
+
+dpnorm_status dpnorm_hutch_grouped_noalloc(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt, int64_t B,
+                                           int64_t T, int64_t k, float* n, int accumulate, float* c, float C,
+                                           hipStream_t stream) {
+  // the plan must fit the static scratch (sharing A if that fits, else not)
+  // before the device is touched
+  HutchCall hc;
+  const dpnorm_status st = build_hutch(layers, L, dt, B, T, k, true, true, HUTCH_DENSE, hc);
+  if (st != DPNORM_OK) return st;
+  if (hc.bytes > DPNORM_STATIC_SCRATCH_BYTES) {
+    HutchCall plain;
+    if (build_hutch(layers, L, dt, B, T, k, true, false, HUTCH_DENSE, plain) != DPNORM_OK ||
+        plain.bytes > DPNORM_STATIC_SCRATCH_BYTES)
+      return DPNORM_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const dpnorm_status sst = static_scratch(stream, &ws);
+  if (sst != DPNORM_OK) return sst;
+  return hutch_impl(layers, L, dt, B, T, k, n, accumulate, c, C, ws, DPNORM_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 dpnorm_status dpnorm_hutch_sign(const void* A, const void* G, const uint32_t* S_bits, dpnorm_dtype dt, int64_t B,

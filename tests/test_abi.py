@@ -253,3 +253,23 @@ def test_exact_checks(lib):
                             None) == _lib.ERR_NULL
     assert lib.dpnorm_exact(A_ADDR, G_ADDR, _lib.BF16, 2, 100, 64, 32, 0, A_ADDR, 0, WS_ADDR, nb.value,
                             None) == _lib.ERR_VALUE
+
+
+def test_noalloc_rejects_plans_beyond_the_static_scratch(lib):
+    """dpnorm_hutch_grouped_noalloc checks its plan against the static scratch
+    before it touches the device: the 112-projection Llama-shaped stack at
+    B=4, T=4096 needs far more than 64 MiB and is rejected, and so are
+    invalid sizes."""
+    shapes = [(2048, 2048), (2048, 512), (2048, 512), (2048, 2048), (2048, 8192), (2048, 8192), (8192, 2048)] * 16
+    arr = (_lib.Layer * len(shapes))()
+    for j, (d, p) in enumerate(shapes):
+        arr[j] = _lib.Layer(A_ADDR + (j << 32), G_ADDR + (j << 32), P_ADDR + (j << 32), d, p)
+    nb = C.c_size_t(0)
+    assert lib.dpnorm_hutch_grouped_workspace(arr, len(shapes), _lib.BF16, 4, 4096, 32, C.byref(nb)) == _lib.OK
+    assert nb.value > _lib.STATIC_SCRATCH_BYTES
+    assert lib.dpnorm_hutch_grouped_noalloc(arr, len(shapes), _lib.BF16, 4, 4096, 32, N_ADDR, 0, None, 1.0,
+                                            None) == _lib.ERR_WORKSPACE
+    assert lib.dpnorm_hutch_grouped_noalloc(arr, 1, _lib.BF16, 4, 4096, 65, N_ADDR, 0, None, 1.0,
+                                            None) == _lib.ERR_SIZE
+    assert lib.dpnorm_hutch_grouped_noalloc(None, 1, _lib.BF16, 4, 4096, 32, N_ADDR, 0, None, 1.0,
+                                            None) == _lib.ERR_NULL
