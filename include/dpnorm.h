@@ -64,12 +64,23 @@ typedef enum dpnorm_status {
   DPNORM_ERR_HIP = 7          /* a kernel launch or HIP call failed */
 } dpnorm_status;
 
-typedef enum dpnorm_dtype { DPNORM_F32 = 0, DPNORM_BF16 = 1 } dpnorm_dtype;
+/* The *_RANGE_MIN_ / *_RANGE_MAX_ enumerators of the two enums callers pass
+ * in are range markers, not valid values: they make every int32 a value of
+ * the type, so that an unknown value is rejected with DPNORM_ERR_DTYPE
+ * instead of being undefined in the library's C++. */
+typedef enum dpnorm_dtype {
+  DPNORM_F32 = 0,
+  DPNORM_BF16 = 1,
+  DPNORM_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  DPNORM_DTYPE_RANGE_MAX_ = 2147483647
+} dpnorm_dtype;
 
 typedef enum dpnorm_route {
   DPNORM_EXACT_AUTO = 0,      /* explicit when d*p <= T*T, else Gram */
   DPNORM_EXACT_EXPLICIT = 1,  /* sum of squares of A^T G tiles (never stored) */
-  DPNORM_EXACT_GRAM = 2       /* <A A^T, G G^T> over T x T tiles (never stored) */
+  DPNORM_EXACT_GRAM = 2,      /* <A A^T, G G^T> over T x T tiles (never stored) */
+  DPNORM_ROUTE_RANGE_MIN_ = -2147483647 - 1,
+  DPNORM_ROUTE_RANGE_MAX_ = 2147483647
 } dpnorm_route;
 
 /* One linear-like layer of a grouped call: device pointers A [B][T][d],

@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <numeric>
 #include <vector>
@@ -108,18 +109,23 @@ size_t packed_units(const PassPlan& pl, int64_t rows) {
 void form_groups(PassPlan& pl, const std::vector<PassLayer>& L) {
   const int nl = (int)L.size();
   pl.groups.clear();
-  std::vector<int> done(nl, 0);
+  // layers reading one X2, in order of their first layer, each in call order
+  // (one pass with a map, so a call over many layers plans in O(L log L))
+  std::vector<std::vector<int>> lists;
+  std::map<std::pair<uintptr_t, int64_t>, int> list_of;
   for (int l = 0; l < nl; ++l) {
-    if (done[l]) continue;
-    std::vector<int> same{l};
-    done[l] = 1;
     if (pl.fuse && L[l].X2) {
-      for (int m = l + 1; m < nl; ++m)
-        if (!done[m] && L[m].X2 == L[l].X2 && L[m].w2 == L[l].w2) {
-          same.push_back(m);
-          done[m] = 1;
-        }
+      const auto key = std::make_pair((uintptr_t)L[l].X2, L[l].w2);
+      const auto it = list_of.find(key);
+      if (it != list_of.end()) {
+        lists[it->second].push_back(l);
+        continue;
+      }
+      list_of.emplace(key, (int)lists.size());
     }
+    lists.push_back({l});
+  }
+  for (const std::vector<int>& same : lists) {
     size_t at = 0;
     while (at < same.size()) {
       int take = (int)std::min<size_t>(same.size() - at, 6 / pl.NCB > 0 ? 6 / pl.NCB : 1);

@@ -25,8 +25,12 @@ def pytest_runtest_setup(item):
 
 @pytest.fixture(scope="session")
 def lib():
-    """The built C-ABI library (built here if nothing is built yet)."""
+    """The built C-ABI library (built here if nothing is built yet), or the
+    one DPNORM_TEST_LIB names (the host-layer build under sanitizers)."""
     from sample_grad_norms_amd import _lib
+    other = os.environ.get("DPNORM_TEST_LIB")
+    if other:
+        return _lib.load(other)
     if not os.path.exists(_lib.LIB_PATH):
         from sample_grad_norms_amd import build as _build
         _build.build_library()
