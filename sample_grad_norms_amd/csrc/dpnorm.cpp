@@ -144,8 +144,15 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   const int nl = (int)L.size();
   pl.Tpad = (pl.T + kRowsK1 - 1) / kRowsK1 * kRowsK1;
   pl.nch = (int)((pl.T + 31) / 32);
-  // bf16 stage 1 takes 64-row items when 128-row items would leave CUs idle
-  pl.rows1 = pl.bf16 && (int64_t)nl * pl.B * (pl.Tpad / kRowsK1) < kMinItems ? kRowsK1Small : kRowsK1;
+  // bf16 stage 1 takes smaller items when 128-row items would leave CUs
+  // idle: 64 rows on two waves; 32 rows over four waves that split the
+  // columns when even those leave CUs idle and the LDS holds four chunks of W
+  // per stage (NCB HL <= 2). (Four-wave K-split groups take one CU each, so
+  // where 64-row items already fill the CUs they would run in two rounds.)
+  const int64_t items128 = (int64_t)nl * pl.B * (pl.Tpad / kRowsK1);
+  pl.rows1 = kRowsK1;
+  if (pl.bf16 && items128 < kMinItems)
+    pl.rows1 = 2 * items128 < kMinItems && pl.NCB * pl.HL <= 2 ? kRowsK1Tiny : kRowsK1Small;
   pl.rbs = (int)(pl.Tpad / pl.rows1);
   pl.cols2 = pl.bf16 ? kColsK2Bf16 : kColsK2F32;
   form_groups(pl, L);
@@ -532,7 +539,7 @@ dpnorm_status build_hutch(const dpnorm_layer* layers, int64_t L, dpnorm_dtype dt
       pl.ld = sign ? (k + 31) / 32 : k;
       pl.ncols = (int)k;
     }
-    items1 += B * ((T + kRowsK1Small - 1) / kRowsK1Small);
+    items1 += B * ((T + kRowsK1Tiny - 1) / kRowsK1Tiny);
     items2 += B * ((pl.w2 + kColsK2F32 - 1) / kColsK2F32) * 64;
   }
   if (items1 >= ((int64_t)1 << 31) || items2 >= ((int64_t)1 << 31)) return DPNORM_ERR_SIZE;

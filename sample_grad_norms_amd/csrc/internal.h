@@ -18,7 +18,8 @@
 namespace dpn {
 
 constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x 32)
-constexpr int kRowsK1Small = 64;  // same with 2 waves (bf16, when 128-row items leave CUs idle)
+constexpr int kRowsK1Small = 64;  // same with 2 waves (bf16)
+constexpr int kRowsK1Tiny = 32;   // bf16, 4 waves splitting the columns of 32 rows (when 128-row items leave CUs idle)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 256;   // elements of a Y tile per split-T reduction work group (one wave)

@@ -213,70 +213,89 @@ constexpr int kK1Cols = 64;                          // columns of X1 per stage 
 constexpr int kK1XDma = 32 * kK1Cols * 2 / 1024;     // 1 KB X1 instructions per wave per stage (its 32 rows)
 constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
 
-// NW waves, 32 NW rows per item: 4 (128 rows) normally, 2 (64 rows) when
-// 128-row items would leave CUs idle.
-// RAW (HL = 1): W is the caller's bf16 [w1][NC] matrix. A stage's 64 rows
+// NW waves. KS = 1: wave w owns rows 32 w .. 32 w + 31 of a 32 NW-row item
+// (128 rows normally, 64 when 128-row items would leave CUs idle). KS = NW
+// (K split, for calls with fewer items still): all waves share one 32-row
+// item and stage st holds NW consecutive 64-column chunks of it, one per
+// wave (chunk NW st + w, counted from the group's first chunk), each with its
+// 64 rows of W; at the end the waves' partial sums are added through LDS in
+// wave order, so the result does not depend on timing.
+// RAW (HL = 1): W is the caller's bf16 [w1][NC] matrix. A chunk's 64 rows
 // of it are one contiguous run, loaded as they are (rows past w1 from a zero
 // row) and kept row-major in LDS; each B operand is two transposing reads
 // (rows 32 kk + 8 g .. + 3 and + 4 .. + 7 of column 16 jb + n), so the call
 // needs no packed copy of W. IMPL: implicit mode (items and record not in
 // memory; always RAW).
-template <int NCB, int HL, int NW, bool RAW, bool IMPL>
+template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
 __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   static_assert(!RAW || HL == 1, "W read in place is bf16");
   static_assert(!IMPL || RAW, "implicit mode reads W in place");
+  static_assert(KS == 1 || KS == NW, "the K split spreads one 32-row item over all waves");
   constexpr int NC = 16 * NCB;
-  constexpr int kRows = 32 * NW;
-  constexpr int kK1XBytes = kRows * kK1Cols * 2;         // X1 bytes per stage (16 KB for 4 waves)
-  constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per stage
-  constexpr int kStage = kK1XBytes + kWBlocks * 1024;
-  constexpr int kPerWave = kK1XDma + kWBlocks / NW;      // loads every wave issues per stage (at least)
+  constexpr int kRows = 32 * NW / KS;                    // rows per item
+  constexpr int kK1XBytes = NW * 32 * kK1Cols * 2;       // X1 bytes per stage (16 KB for 4 waves)
+  constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per chunk
+  constexpr int kStage = kK1XBytes + KS * kWBlocks * 1024;
+  constexpr int kPerWave = kK1XDma + KS * kWBlocks / NW; // loads every wave issues per stage (at least)
+  static_assert(kK1Bufs * kStage <= 160 * 1024, "the stage ring must fit the LDS of one work group");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kK1Bufs * kStage];
   const int4 it = stage1_item<IMPL>(a, blockIdx.x);
   const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, rb = it.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const int rg = KS == 1 ? wv : 0;                       // this wave's 32-row group within the item
+  const int kq = KS == 1 ? 0 : wv;                       // this wave's chunk within a stage
   const int w = L->w1, T = a.T;
   const int r0 = rb * kRows;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
   const uint4* Wp = (const uint4*)L->W + i * L->w_stride_b + lane;  // packed to an even number of K steps
   const uint16_t* Wr = (const uint16_t*)L->W;                       // RAW: [w][NC] as the caller holds it
-  const int nst = (w + kK1Cols - 1) / kK1Cols;
-  const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nst);  // first column stage of this group
+  const int nch = (w + kK1Cols - 1) / kK1Cols;                      // 64-column chunks
+  const int nst = (nch + KS - 1) / KS;
+  const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nch);   // first chunk of this group
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
   // X1 source of this lane: instruction j of wave wv fills LDS rows
   // 8 (4 wv + j) + lane / 8 at unit position lane % 8, which holds global
-  // unit (lane % 8) ^ (row % 8). Rows past T and columns past w read the last
-  // valid row / unit instead: those values only ever meet zero rows of A or
-  // zero rows of W, so they contribute nothing.
+  // unit (lane % 8) ^ (row % 8) of row 32 rg + 8 j + lane / 8 of the item.
+  // Rows past T and columns past w read the last valid row / unit instead:
+  // those values only ever meet zero rows of A or zero rows of W, so they
+  // contribute nothing.
   const int urow0 = 32 * wv + (lane >> 3);
   const int gunit = (lane & 7) ^ (urow0 & 7);  // row % 8 is the same for all j (rows step by 8)
+  const int grow0 = r0 + 32 * rg + (lane >> 3);
+  auto chunk_of = [&](int st, int q) {         // chunk read by slot q of stage st (nch or more: none)
+    const int c = KS * st + q;
+    if (c >= nch) return nch;
+    return c + rot < nch ? c + rot : c + rot - nch;
+  };
   auto dma = [&](int st) {
     if (st >= nst) return;
     const uint32_t buf = lds_base + (uint32_t)((st % kK1Bufs) * kStage);
-    const int cst = st + rot < nst ? st + rot : st + rot - nst;  // column stage read at step st
-    int col = cst * kK1Cols + gunit * 8;
+    const int cx = chunk_of(st, kq);
+    int col = min(cx, nch - 1) * kK1Cols + gunit * 8;
     col = col < w ? col : w - 8;
 #pragma unroll
     for (int j = 0; j < kK1XDma; ++j) {
-      int row = r0 + urow0 + 8 * j;
+      int row = grow0 + 8 * j;
       row = row < T ? row : T - 1;
       dma16_stream(X + (int64_t)row * w + col, buf + (uint32_t)((wv * kK1XDma + j) * 1024));
     }
 #pragma unroll
-    for (int m0 = 0; m0 < (kWBlocks + NW - 1) / NW; ++m0) {
-      const int m = NW * m0 + wv;
-      if (RAW) {  // instruction m: rows 64 cst + (512 / NC) m .., 2 NCB lanes of 16 bytes a row
-        if (m < kWBlocks) {
-          const int row = 64 * cst + m * (512 / NC) + lane / (2 * NCB);
+    for (int m0 = 0; m0 < (KS * kWBlocks + NW - 1) / NW; ++m0) {
+      const int m = NW * m0 + wv;                // W block m: chunk slot m / kWBlocks, block m % kWBlocks
+      if (m < KS * kWBlocks) {
+        const int q = m / kWBlocks, mb = m % kWBlocks;
+        const int cw = chunk_of(st, q);
+        if (RAW) {  // block mb: rows 64 cw + (512 / NC) mb .., 2 NCB lanes of 16 bytes a row
+          const int row = 64 * cw + mb * (512 / NC) + lane / (2 * NCB);
           const void* src =
               row < w ? (const void*)(Wr + (int64_t)row * NC + 8 * (lane % (2 * NCB))) : (const void*)g_zero16;
           dma16(src, buf + (uint32_t)(kK1XBytes + m * 1024));
+        } else {
+          dma16(Wp + ((int64_t)min(cw, nch - 1) * kWBlocks + mb) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
         }
-      } else if (m < kWBlocks) {
-        dma16(Wp + ((int64_t)cst * kWBlocks + m) * 64, buf + (uint32_t)(kK1XBytes + m * 1024));
       }
     }
   };
@@ -299,13 +318,15 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
     else DPN_WAIT_VMCNT(0);
     block_barrier();
     dma(st + 3);
+    if (KS > 1 && KS * st + kq >= nch) continue;  // no chunk for this wave in the last stage (wave-uniform)
     const unsigned char* buf = lds + (st % kK1Bufs) * kStage;
-    const uint4* wf = (const uint4*)(buf + kK1XBytes) + lane;
+    const uint4* wf = (const uint4*)(buf + kK1XBytes + kq * kWBlocks * 1024) + lane;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       uint4 f[NCB][HL];
       if (RAW) {
-        const unsigned char* wr = buf + kK1XBytes + (32 * kk + 8 * g + (n >> 2)) * (NC * 2) + (n & 3) * 8;
+        const unsigned char* wr =
+            buf + kK1XBytes + kq * kWBlocks * 1024 + (32 * kk + 8 * g + (n >> 2)) * (NC * 2) + (n & 3) * 8;
 #pragma unroll
         for (int jb = 0; jb < NCB; ++jb) {
           const uint2 lo = lds_read_tr16(wr + 32 * jb);
@@ -330,8 +351,34 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
     }
   }
 
-  if (r0 + 32 * wv >= T) return;  // chunk past the sequence: stage 2 never reads it
-  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32 + wv) * L->vstride + lane;
+  if (KS > 1) {
+    // partial sums of waves 1 .. KS - 1 through LDS (every wave is past its
+    // last LDS read once all have reached this barrier), added by wave 0 in
+    // wave order
+    block_barrier();
+    float* red = (float*)lds;
+    if (wv > 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[(((wv - 1) * 2 + mt) * NCB + jb) * 256 + r * 64 + lane] = acc[mt][jb][r];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int q = 1; q < KS; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mt][jb][r] += red[(((q - 1) * 2 + mt) * NCB + jb) * 256 + r * 64 + lane];
+  }
+
+  if (r0 + 32 * rg >= T) return;  // chunk past the sequence: stage 2 never reads it
+  uint4* out = (uint4*)L->V + ((int64_t)i * (a.Tpad / 32) + r0 / 32 + rg) * L->vstride + lane;
 #pragma unroll
   for (int jb = 0; jb < NCB; ++jb) {
     uint32_t hi[8], lo[8];
@@ -708,20 +755,27 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NW, int HL, bool RAW, bool IMPL>
-static void rowproj_bf16_ncb(const StageArgs& a, int NCB, hipStream_t s) {
-  const dim3 grid(a.n_items), blk(64 * NW);
-  if (NCB == 1) hipLaunchKernelGGL((k_rowproj_bf16<1, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
-  else if (NCB == 2) hipLaunchKernelGGL((k_rowproj_bf16<2, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
-  else hipLaunchKernelGGL((k_rowproj_bf16<4, HL, NW, RAW, IMPL>), grid, blk, 0, s, a);
+// The K split carries KS chunks of W per stage: only NCB HL <= 2 fits the LDS
+// (the host takes 64-row items for wider W), so no other is instantiated.
+template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
+static void rowproj_bf16_one(const StageArgs& a, hipStream_t s) {
+  if constexpr (KS == 1 || NCB * HL <= 2)
+    hipLaunchKernelGGL((k_rowproj_bf16<NCB, HL, NW, RAW, IMPL, KS>), dim3(a.n_items), dim3(64 * NW), 0, s, a);
 }
 
-template <int NW>
+template <int NW, int HL, bool RAW, bool IMPL, int KS>
+static void rowproj_bf16_ncb(const StageArgs& a, int NCB, hipStream_t s) {
+  if (NCB == 1) rowproj_bf16_one<1, HL, NW, RAW, IMPL, KS>(a, s);
+  else if (NCB == 2) rowproj_bf16_one<2, HL, NW, RAW, IMPL, KS>(a, s);
+  else rowproj_bf16_one<4, HL, NW, RAW, IMPL, KS>(a, s);
+}
+
+template <int NW, int KS>
 static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, bool raw, bool implicit, hipStream_t s) {
-  if (implicit) rowproj_bf16_ncb<NW, 1, true, true>(a, NCB, s);
-  else if (raw) rowproj_bf16_ncb<NW, 1, true, false>(a, NCB, s);
-  else if (HL == 1) rowproj_bf16_ncb<NW, 1, false, false>(a, NCB, s);
-  else rowproj_bf16_ncb<NW, 2, false, false>(a, NCB, s);
+  if (implicit) rowproj_bf16_ncb<NW, 1, true, true, KS>(a, NCB, s);
+  else if (raw) rowproj_bf16_ncb<NW, 1, true, false, KS>(a, NCB, s);
+  else if (HL == 1) rowproj_bf16_ncb<NW, 1, false, false, KS>(a, NCB, s);
+  else rowproj_bf16_ncb<NW, 2, false, false, KS>(a, NCB, s);
 }
 
 hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool raw, bool implicit,
@@ -731,8 +785,9 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
   if (implicit && a.rbs < 1) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
   if (bf16) {
-    if (rows1 == kRowsK1) rowproj_bf16_nw<4>(a, NCB, HL, raw, implicit, s);
-    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2>(a, NCB, HL, raw, implicit, s);
+    if (rows1 == kRowsK1) rowproj_bf16_nw<4, 1>(a, NCB, HL, raw, implicit, s);
+    else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2, 1>(a, NCB, HL, raw, implicit, s);
+    else if (rows1 == kRowsK1Tiny && NCB * HL <= 2) rowproj_bf16_nw<4, 4>(a, NCB, HL, raw, implicit, s);
     else return hipErrorInvalidValue;
   } else {
     if (rows1 != kRowsK1) return hipErrorInvalidValue;
