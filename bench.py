@@ -91,6 +91,50 @@ def cpu_baseline(layers, B, T, n_layers):
             "host": host_cpu()}
 
 
+def oracle_per_config():
+    """The fp64 oracle on the other workloads, each once on its full inputs
+    (copied to the host and converted to float64 first; only the oracle's
+    arithmetic is timed): the tiny fp32 layer (Hutchinson, exact, clip), the
+    single layer (Hutchinson; the exact norm by the Gram route), Hutch++ and
+    the long-context layer (Hutchinson; the exact norm by the explicit route,
+    about 1.1 TFLOP of fp64). Rates in samples * tokens / s of that work."""
+    import oracle
+    import torch
+    import workloads
+    dev = torch.device("cuda:0")
+
+    def run(name, B, T, parts):
+        out = {}
+        for what, fn in parts:
+            t0 = time.perf_counter()
+            fn()
+            out[what] = time.perf_counter() - t0
+        total = sum(out.values())
+        return {"value": B * T / total, "unit": "samples·tokens/s", "seconds": out, "workload": name}
+
+    res = {}
+    pr = workloads.config1(device=dev)
+    A, G, P = oracle.to_f64(pr.A), oracle.to_f64(pr.G), oracle.to_f64(pr.P)
+    res["tiny_fp32_B2_T128_d64_p64_k8"] = run(pr.name, 2, 128, [
+        ("hutch", lambda: oracle.hutch(A, G, P)), ("exact_explicit", lambda: oracle.exact_explicit(A, G)),
+        ("clip", lambda: oracle.clip_factors(oracle.hutch(A, G, P), 1.0))])
+    pr = workloads.config2(device=dev)
+    A, G, P = oracle.to_f64(pr.A), oracle.to_f64(pr.G), oracle.to_f64(pr.P)
+    res["single_layer_B8_T1024_d2048_p2048_k32"] = run(pr.name, 8, 1024, [
+        ("hutch", lambda: oracle.hutch(A, G, P)), ("exact_gram", lambda: oracle.exact_gram(A, G))])
+    pr = workloads.config4(device=dev)
+    A, G, S, P = oracle.to_f64(pr.A), oracle.to_f64(pr.G), oracle.to_f64(pr.S), oracle.to_f64(pr.P)
+    res["hutchpp_B4_T4096_d2048_p2048_k32"] = run(pr.name, 4, 4096, [("hutchpp", lambda: oracle.hutchpp(A, G, S, P))])
+    del A, G, S, P
+    pr = workloads.config5(device=dev)
+    A, G, P = oracle.to_f64(pr.A), oracle.to_f64(pr.G), oracle.to_f64(pr.P)
+    del pr
+    res["long_context_B1_T32768_d2048_p8192_k32"] = run("config5_bf16_B1_T32768_d2048_p8192_k32", 1, 32768, [
+        ("hutch", lambda: oracle.hutch(A, G, P)), ("exact_explicit", lambda: oracle.exact_explicit(A, G))])
+    del A, G, P
+    return res
+
+
 def host_cpu() -> str:
     """The host's CPU model and logical CPU count (from /proc/cpuinfo)."""
     model, n = "unknown", 0
@@ -286,6 +330,35 @@ def lora_stack(args):
     return out
 
 
+def estimator_variance(pr, ws, wsh, draws=200):
+    """Relative variance of n_hat / n over `draws` fresh draws of (S, P) for
+    Hutch++ and of P for Hutchinson at the same budget k on the Hutch++
+    workload (n from dpnorm_exact), and their ratio per sample."""
+    import math
+    import torch
+    import sample_grad_norms_amd as dp
+    dev = pr.A.device
+    B, T, d = pr.A.shape
+    p, k = pr.G.shape[2], pr.k
+    ms_, mt = dp.hutchpp_split(k)
+    n = dp.exact(pr.A, pr.G).double()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4_000_999)
+    hu = torch.empty(draws, B, device=dev)
+    hp = torch.empty(draws, B, device=dev)
+    for r in range(draws):
+        P = (torch.randn(p, k, generator=gen, device=dev) / math.sqrt(k)).to(torch.bfloat16)
+        S = torch.randn(p, ms_, generator=gen, device=dev).to(torch.bfloat16)
+        Pt = (torch.randn(p, mt, generator=gen, device=dev) / math.sqrt(mt)).to(torch.bfloat16)
+        dp.hutch(pr.A, pr.G, P, out=hu[r], workspace=wsh)
+        dp.hutchpp(pr.A, pr.G, S, Pt, k=k, out=hp[r], workspace=ws)
+    torch.cuda.synchronize()
+    vu = (hu.double() / n).var(dim=0)
+    vp = (hp.double() / n).var(dim=0)
+    return {"draws": draws, "hutch_rel_var": vu.tolist(), "hutchpp_rel_var": vp.tolist(),
+            "hutch_over_hutchpp": (vu / vp).tolist()}
+
+
 def extras(args):
     """Other workloads: single-layer Hutchinson, Hutch++ and the exact
     comparator, each timed the same way."""
@@ -352,7 +425,8 @@ def extras(args):
     out["hutchpp_B4_T4096_d2048_p2048_k32"] = {
         "hutchpp_ms": ms, "hutchpp_samples_tokens_per_s": B * T / (ms * 1e-3),
         "hutchpp_hbm_gbs_3_streams": byt / ms / 1e6, "hutch_same_inputs_ms": msh,
-        "hutchpp_over_hutch_time": ms / msh}
+        "hutchpp_over_hutch_time": ms / msh,
+        "variance_over_draws": estimator_variance(sets[0], ws, wsh)}
     # the ghost-clipping (Gram) route on the same T = 4096 inputs, beside Hutchinson
     wsg = torch.empty(dp.exact_workspace(torch.bfloat16, B, T, d, p, "gram"), dtype=torch.uint8, device=dev)
     msg = timed(lambda: dp.exact(sets[0].A, sets[0].G, route="gram", workspace=wsg), 10, 10)
@@ -485,6 +559,8 @@ def main():
         rec["extras"].update(extras(args))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(layers, B, T, max(1, min(16, args.cpu_layers)))
+        del layers, projs, ws
+        rec["cpu_baseline"]["per_config"] = oracle_per_config()
     print(json.dumps(rec), flush=True)
 
 
