@@ -166,9 +166,20 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
       pl.group_of[g.members[j]] = gi;
       pl.jb0[g.members[j]] = (int)j * pl.NCB;
     }
-    g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
-    base_items += pl.B * g.ubs;
+    base_items += pl.B * ((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
   }
+  // A bf16 call whose 512-column items, split into pieces of at least 512
+  // rows, would leave CUs idle takes items of 256 columns on two waves: twice
+  // the items per split, so fewer and longer splits (and fewer partial tiles)
+  // for as many work groups.
+  if (pl.bf16 && base_items < kTargetItems &&
+      base_items * std::min<int64_t>((kTargetItems + base_items - 1) / base_items,
+                                     std::max(1, pl.nch / kMinChunksPerSplit)) < kMinItems) {
+    pl.cols2 = kColsK2Bf16Narrow;
+    base_items = 0;
+    for (const PassGroup& g : pl.groups) base_items += pl.B * ((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
+  }
+  for (PassGroup& g : pl.groups) g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
   // Split T when there are few (layer, sample, column block) items: more
   // splits fill the CUs but write and re-read more partial tiles, so splits
   // keep at least 512 rows, or 256 while the launch would leave CUs idle.
@@ -402,7 +413,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {
     st.items = items2 + pl.class_begin[c];
     st.n_items = pl.class_end[c] - pl.class_begin[c];
-    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.direct(), impl, s));
+    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.cols2, pl.direct(), impl, s));
     DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
     if (pl.needs_ysum() && ysum) {
       DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, impl, s));

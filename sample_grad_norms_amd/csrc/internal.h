@@ -21,6 +21,7 @@ constexpr int kRowsK1 = 128;      // rows of X1 per stage-1 work item (4 waves x
 constexpr int kRowsK1Small = 64;  // same with 2 waves (bf16)
 constexpr int kRowsK1Tiny = 32;   // bf16, 4 waves splitting the columns of 32 rows (when 128-row items leave CUs idle)
 constexpr int kColsK2Bf16 = 512;  // columns of X2 per stage-2 work item, bf16 (4 waves x 128)
+constexpr int kColsK2Bf16Narrow = 256;  // same on 2 waves, for calls that split T
 constexpr int kColsK2F32 = 256;   // same, fp32 (4 waves x 64)
 constexpr int kYsumChunk = 256;   // elements of a Y tile per split-T reduction work group (one wave)
 constexpr int kPrepChunk = 160;   // layers described per prepare launch (a ~24 KB kernel-argument table; one launch covers a 1B-class model)
@@ -106,7 +107,9 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).
-hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, bool implicit, hipStream_t s);
+// cols: columns of X2 per item (kColsK2Bf16 or kColsK2Bf16Narrow for bf16; kColsK2F32).
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, int cols, bool direct, bool implicit,
+                            hipStream_t s);
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, bool implicit, hipStream_t s);
 // work groups of the split-T reduction per (layer, sample, column block)
 inline int ysum_chunks(int cols_per_block, int NCB) { return (cols_per_block * 16 * NCB + kYsumChunk - 1) / kYsumChunk; }

@@ -454,14 +454,15 @@ __global__ void __launch_bounds__(256) k_rowproj_f32(StageArgs a) {
 // else:   the tile is stored to Ypart[ts][i][u][NC].
 // Lane l's accumulator (e, jb, r) is Y[u0 + ustride (4 (l/16) + r) + e][16 jb + l%16].
 // ---------------------------------------------------------------------------
-template <int NCB, int NE, bool DIRECT>
+template <int NCB, int NE, bool DIRECT, int NW = 4>
 __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const LayerRec* L, f32x4_t (&acc)[NE][NCB],
                                                    int i, int ub, int ts, int wave_u0, int ustride, int lane,
                                                    int wv) {
+  static_assert(NW == 2 || NW == 4, "work groups of two or four waves");
   constexpr int NC = 16 * NCB;
   const int n = lane & 15, g = lane >> 4;
   if (DIRECT) {
-    __shared__ double red[4][2];
+    __shared__ double red[NW][2];
     const int split = L->split;
     double s0 = 0.0, s1 = 0.0;
 #pragma unroll
@@ -481,10 +482,14 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
       red[wv][1] = s1;
     }
     __syncthreads();
-    if (threadIdx.x == 0)
-      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub] =
-          make_double2((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]),
-                       (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]));
+    if (threadIdx.x == 0) {
+      double r0 = red[0][0] + red[1][0], r1 = red[0][1] + red[1][1];
+      if (NW == 4) {
+        r0 += red[2][0] + red[3][0];
+        r1 += red[2][1] + red[3][1];
+      }
+      a.partials[(int64_t)i * a.slots_per_sample + L->slot_base + ub] = make_double2(r0, r1);
+    }
   } else {
     const int w = L->w2;
     float* Y = L->Ypart + ((int64_t)ts * a.B + i) * w * NC;
@@ -502,29 +507,36 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2, bf16: Y = X2^T V over the chunks of one T split, for 512 columns
-// of X2 (4 waves x 128).
+// Stage 2, bf16: Y = X2^T V over the chunks of one T split, for 128 NW
+// columns of X2 (NW waves x 128: 512 columns normally, 256 on two waves for
+// calls that split T, so that they need half the splits).
 //
 // Each 32-row chunk of X2 (32 rows x 1 KB) and its V fragments are streamed
-// into LDS with direct global-to-LDS loads, as in stage 1 (wave w loads rows
-// 8w..8w+7 of the chunk and one or two 1 KB V blocks), with three chunks in
-// flight while one is multiplied. A lane then reads 8 rows (slot_row) of its
+// into LDS with direct global-to-LDS loads, as in stage 1 (wave w issues
+// eight 1 KB loads of the chunk's rows, one row of 512 columns or two of 256
+// each, and a share of the 1 KB V blocks), with two or three chunks in flight
+// while one is multiplied. A lane then reads 8 rows (slot_row) of its
 // 8 consecutive columns from LDS, transposes the 8 x 8 block in registers so
 // the contraction index runs along the MFMA K slots, and multiplies it
 // against the hi and lo fragments of V. Rows past T and columns past w load
 // the last valid row / column and are zeroed after the LDS read.
 // ---------------------------------------------------------------------------
 constexpr int kK2Rows = 32;                              // rows of X2 per stage (one MFMA K step)
-constexpr int kK2XBytes = kK2Rows * kColsK2Bf16 * 2;     // X2 bytes per stage (32 KB)
 
 
-template <int NCB, bool DIRECT, bool IMPL>
-__global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
+template <int NCB, bool DIRECT, bool IMPL, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) k_tcontract_bf16(StageArgs a) {
+  static_assert(NW == 2 || NW == 4, "work groups of two or four waves");
+  constexpr int kCols = 128 * NW;                        // columns of X2 per item
+  constexpr int kRowBytes = 2 * kCols;                   // one row of the item in LDS
+  constexpr int kRowsPerDma = 1024 / kRowBytes;          // rows per 1 KB load (1 or 2)
+  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kK2XBytes = kK2Rows * kRowBytes;         // X2 bytes per stage (32 or 16 KB)
   constexpr int kVBlocks = 2 * NCB;                      // 1 KB V fragment blocks per chunk
   constexpr int kStage = kK2XBytes + kVBlocks * 1024;
-  constexpr int kBufs = NCB <= 2 ? 4 : 3;                // LDS ring (stages in flight: kBufs - 1)
-  constexpr int kXDma = kK2Rows / 4;                     // 1 KB X2 rows per wave per stage
-  constexpr int kP = kXDma + kVBlocks / 4;               // loads every wave issues per stage (at least)
+  constexpr int kBufs = NW == 4 ? (NCB <= 2 ? 4 : 3) : (4 * kStage <= 80 * 1024 ? 4 : 3);  // LDS ring
+  constexpr int kXDma = kK2XBytes / 1024 / NW;           // 1 KB X2 loads per wave per stage (8)
+  constexpr int kP = kXDma + kVBlocks / NW;              // loads every wave issues per stage (at least)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
   const int4 it = stage2_item<IMPL>(a, xcd_item(blockIdx.x, (uint32_t)a.n_items));
   const LayerRec* L = layer_rec<IMPL>(a, it.x);
@@ -532,9 +544,11 @@ __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
   const int w = L->w2, T = a.T;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int wave_u0 = ub * kColsK2Bf16 + wv * 128;
+  const int wave_u0 = ub * kCols + wv * 128;
   const bool uok = wave_u0 + 8 * n < w;
-  const int dcol = min(ub * kColsK2Bf16 + 8 * lane, w - 8);  // this lane's 16 bytes of each loaded row
+  // this lane's 16 bytes of each loaded row, and its row within a 1 KB load
+  const int dcol = min(ub * kCols + 8 * (lane % kLanesPerRow), w - 8);
+  const int drow = lane / kLanesPerRow;
   const uint16_t* X = (const uint16_t*)L->X2 + (int64_t)i * T * w + dcol;
   const uint4* V = (const uint4*)L->V + (int64_t)i * (a.Tpad / 32) * (NCB * 2 * 64) + lane;
   const int nch = (T + 31) >> 5;
@@ -548,13 +562,13 @@ __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
     const int c = c0 + st;
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
-      int t = kK2Rows * c + kXDma * wv + j;
+      int t = kK2Rows * c + (kXDma * wv + j) * kRowsPerDma + drow;
       t = t < T ? t : T - 1;
       dma16_stream(X + (int64_t)t * w, buf + (uint32_t)((kXDma * wv + j) * 1024));
     }
 #pragma unroll
-    for (int m0 = 0; m0 < (kVBlocks + 3) / 4; ++m0) {
-      const int m = 4 * m0 + wv;
+    for (int m0 = 0; m0 < (kVBlocks + NW - 1) / NW; ++m0) {
+      const int m = NW * m0 + wv;
       if (m < kVBlocks) dma16(V + ((int64_t)c * kVBlocks + m) * 64, buf + (uint32_t)(kK2XBytes + m * 1024));
     }
   };
@@ -581,7 +595,7 @@ __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int r = slot_row(g, s);
-      const uint4 x = *(const uint4*)(buf + r * 1024 + wv * 256 + n * 16);
+      const uint4 x = *(const uint4*)(buf + r * kRowBytes + wv * 256 + n * 16);
       raw[s] = (uok && t0 + r < T) ? x : z;
     }
     uint4 bv[NCB][2];
@@ -598,7 +612,7 @@ __global__ void __launch_bounds__(256) k_tcontract_bf16(StageArgs a) {
 #pragma unroll
         for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = mfma_bf16(op[e], bv[jb][h], acc[e][jb]);
   }
-  tcontract_epilogue<NCB, 8, DIRECT>(a, L, acc, i, ub, ts, wave_u0, 8, lane, wv);
+  tcontract_epilogue<NCB, 8, DIRECT, NW>(a, L, acc, i, ub, ts, wave_u0, 8, lane, wv);
 }
 
 // ---------------------------------------------------------------------------
@@ -798,10 +812,33 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
   return hipGetLastError();
 }
 
-hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, bool direct, bool implicit, hipStream_t s) {
+hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, int cols, bool direct, bool implicit,
+                            hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   if (implicit && (!bf16 || a.ubs < 1 || (NCB != 1 && NCB != 2 && NCB != 4))) return hipErrorInvalidValue;
+  if (bf16 && cols != kColsK2Bf16 && cols != kColsK2Bf16Narrow) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
+  if (bf16 && cols == kColsK2Bf16Narrow) {  // two-wave work groups of 256 columns
+    const dim3 blk2(128);
+#define DPN_TCN(N, I)                                                                           \
+  do {                                                                                          \
+    if (direct) hipLaunchKernelGGL((k_tcontract_bf16<N, true, I, 2>), grid, blk2, 0, s, a);     \
+    else hipLaunchKernelGGL((k_tcontract_bf16<N, false, I, 2>), grid, blk2, 0, s, a);           \
+  } while (0)
+    if (implicit) {
+      if (NCB == 1) DPN_TCN(1, true);
+      else if (NCB == 2) DPN_TCN(2, true);
+      else DPN_TCN(4, true);
+    } else {
+      if (NCB == 1) DPN_TCN(1, false);
+      else if (NCB == 2) DPN_TCN(2, false);
+      else if (NCB == 3) DPN_TCN(3, false);
+      else if (NCB == 4) DPN_TCN(4, false);
+      else DPN_TCN(6, false);
+    }
+#undef DPN_TCN
+    return hipGetLastError();
+  }
 #define DPN_TC(KER, N)                                                          \
   do {                                                                          \
     if (direct) hipLaunchKernelGGL((KER<N, true>), grid, blk, 0, s, a);         \
