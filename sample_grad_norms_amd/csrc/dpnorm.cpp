@@ -953,9 +953,13 @@ dpnorm_status dpnorm_hutchpp(const void* A, const void* G, const void* S, const 
   if (he == hipSuccess && fuse2)
     he = launch_hpp_ysum_pack((const float*)(base + hc.p1.groups[0].off_Yp), hc.p1.nsplit, (int)B, (int)d, hc.NC1,
                               nx2, stream);
-  if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr, !fuse2);
+  // The sketch pass's split-T sum runs inside the first basis kernel, which
+  // needs the same rows of X for its Gram partials.
+  const bool sum2 = hc.p2.needs_ysum() && hc.p2.groups.size() == 1;
+  if (he == hipSuccess) he = run_pass(hc.p2, hc.l2, base, stream, tr, !fuse2, !sum2);
   if (he == hipSuccess)
-    he = launch_hpp_qr((const float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.mt, P,
+    he = launch_hpp_qr(sum2 ? (const float*)(base + hc.p2.groups[0].off_Yp) : nullptr, hc.p2.nsplit,
+                       (float*)(base + hc.off_x), hc.NC1, (int)B, (int)p, (int)hc.mt, P,
                        dt == DPNORM_BF16 ? SRC_BF16 : SRC_F32, kRankTau, W3, hc.NC3, rk, resid, (int)hc.ms,
                        base + hc.off_qr,
                        fuse3 ? &nx3 : nullptr, stream);

@@ -143,10 +143,13 @@ struct HppNext {
 };
 
 // next == nullptr: W3 is written; else next's packed W (from the same values) and
-// tables are written in its place, and W3 is not.
-hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, float* resid, int ms, void* scratch, const HppNext* next,
-                         hipStream_t s);
+// tables are written in its place, and W3 is not. Ypart == nullptr: X holds
+// the sketch; else X is first written as the split-T sum of Ypart
+// [nsplit][B][p][MP] (in split order, fp64, rounded to fp32), in place of
+// the sketch pass's own split-T sum.
+hipError_t launch_hpp_qr(const float* Ypart, int nsplit, float* X, int MP, int B, int p, int mt, const void* P,
+                         int ptype, float tau, float* W3, int ldw, int32_t* rank, float* resid, int ms, void* scratch,
+                         const HppNext* next, hipStream_t s);
 // The split-T sum of a stored pass, Ypart [nsplit][B][w][NC] fp32 summed in
 // split order (fp64), packed straight into `next`'s projection (the stored
 // Y of that pass is not written), with next's tables.

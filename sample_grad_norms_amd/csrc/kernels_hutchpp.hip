@@ -11,7 +11,10 @@
 // Q is the Q factor of X with positive diagonal (unique for the kept
 // columns), by Cholesky QR in fp64, in two kernels:
 //   k_hpp_gram  : partial X^T X and X^T P over chunks of rows with fp64 MFMA
-//                 (v_mfma_f64_16x16x4), many work groups per sample;
+//                 (v_mfma_f64_16x16x4), many work groups per sample; when
+//                 the sketch pass split T, k_hpp_ysum_gram first sums the
+//                 chunk's rows of X over the split partials (and stores X),
+//                 in place of that pass's own split-T sum;
 //   k_hpp_apply : every work group first sums its sample's partials in a
 //                 fixed order and factors X^T X = R^T R in LDS (right-looking,
 //                 one entry of the Schur complement per thread) with a rank
@@ -35,7 +38,7 @@ namespace dpn {
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMaxTail = 32;
-constexpr int kGramRows = 256;   // rows of X per k_hpp_gram work group
+constexpr int kGramRows = 128;   // rows of X per Gram work group (k_hpp_gram, k_hpp_ysum_gram)
 constexpr int kApplyRows = 64;   // rows of X per k_hpp_apply work group (4 waves x 16)
 constexpr int kMaxYCols = 32;    // columns of a stored sketch pass that k_hpp_ysum_pack takes
 
@@ -72,37 +75,26 @@ __device__ __forceinline__ double x_val(const float* Xi, int p, int row, int c) 
 // Partial tiles of X^T X (upper triangle) and X^T P for kGramRows rows:
 // part [B][nparts][NT][4][64] (the accumulator registers of each tile).
 // The contraction runs over rows: K slot l / 16 is row 4 ks + l / 16.
-template <int MP>
-__global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, int p, int mt,
-                                                  const void* __restrict__ P, int ptype, double* part) {
+// xrow(row, c) gives entry (row, c) of X, 0 past p rows; pv holds the tail
+// projection's entries (row0 + 4 u, 16 tt + n), loaded by the caller.
+template <int MP, class XRow>
+__device__ __forceinline__ void hpp_gram_tiles(const XRow& xrow, const double (&pv)[kGramRows / 16][2], int row0,
+                                               double* part) {
   using H = HppTiles<MP>;
   constexpr int TA = H::TA, NG = H::NG, NT = H::NT;
+  constexpr int U = kGramRows / 4 / 4;  // K steps per wave, loads issued together
   __shared__ double red[4][NT][4][64];
   const int s = blockIdx.x, i = blockIdx.y, nparts = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const float* Xi = X + (int64_t)i * p * MP;
+  const int n = lane & 15;
   f64x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  constexpr int U = kGramRows / 4 / 4;  // K steps per wave, loads issued together
-  double xa[U][TA], pv[U][2];
-  const int row0 = s * kGramRows + 4 * wv * U + g;
+  double xa[U][TA];
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int a = 0; a < TA; ++a) xa[u][a] = x_val<MP>(Xi, p, row0 + 4 * u, 16 * a + n);
-  if (ptype == SRC_BF16) {  // uniform
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<true>(P, p, mt, row0 + 4 * u, 16 * tt + n);
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<false>(P, p, mt, row0 + 4 * u, 16 * tt + n);
-  }
+    for (int a = 0; a < TA; ++a) xa[u][a] = xrow(row0 + 4 * u, 16 * a + n);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -124,6 +116,99 @@ __global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, i
     const int t = e >> 8, j = (e >> 6) & 3, l = e & 63;
     out[e] = (red[0][t][j][l] + red[1][t][j][l]) + (red[2][t][j][l] + red[3][t][j][l]);
   }
+}
+
+// The tail projection's entries a lane of the Gram tiles uses.
+__device__ __forceinline__ void hpp_tail_rows(const void* P, int ptype, int p, int mt, int row0,
+                                              double (&pv)[kGramRows / 16][2]) {
+  constexpr int U = kGramRows / 16;
+  const int n = threadIdx.x & 15;
+  if (ptype == SRC_BF16) {  // uniform
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<true>(P, p, mt, row0 + 4 * u, 16 * tt + n);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) pv[u][tt] = tail_val<false>(P, p, mt, row0 + 4 * u, 16 * tt + n);
+  }
+}
+
+// Row of the first K step of this lane: wave wv takes rows 64 wv .. 64 wv + 63
+// of the chunk, four per K step.
+__device__ __forceinline__ int hpp_gram_row0() {
+  return blockIdx.x * kGramRows + 4 * (threadIdx.x >> 6) * (kGramRows / 16) + ((threadIdx.x & 63) >> 4);
+}
+
+// Gram partials from the stored X [B][p][MP].
+template <int MP>
+__global__ void __launch_bounds__(256) k_hpp_gram(const float* __restrict__ X, int p, int mt,
+                                                  const void* __restrict__ P, int ptype, double* part) {
+  const float* Xi = X + (int64_t)blockIdx.y * p * MP;
+  const int row0 = hpp_gram_row0();
+  double pv[kGramRows / 16][2];
+  hpp_tail_rows(P, ptype, p, mt, row0, pv);
+  hpp_gram_tiles<MP>([&](int row, int c) { return x_val<MP>(Xi, p, row, c); }, pv, row0, part);
+}
+
+// The sketch pass's split-T sum fused with the Gram partials: the work group
+// sums its kGramRows rows of X over the nsplit partial tiles of Ypart
+// [nsplit][B][p][MP] (in split order, fp64, rounded to fp32), stores them to
+// X as the pass's own split-T sum would, and forms the partial tiles from
+// those fp32 values, so X and the tiles are bitwise what the split-T sum
+// followed by k_hpp_gram give.
+template <int MP>
+__global__ void __launch_bounds__(256) k_hpp_ysum_gram(const float* __restrict__ Ypart, int nsplit, int B,
+                                                       float* X, int p, int mt, const void* __restrict__ P,
+                                                       int ptype, double* part) {
+  __shared__ float tile[kGramRows * MP];
+  const int i = blockIdx.y, rb = blockIdx.x * kGramRows;
+  const int row0 = hpp_gram_row0();
+  double pv[kGramRows / 16][2];
+  hpp_tail_rows(P, ptype, p, mt, row0, pv);
+  const int64_t stride = (int64_t)B * p * MP;
+  const float* Y = Ypart + ((int64_t)i * p + rb) * MP;
+  float* Xo = X + ((int64_t)i * p + rb) * MP;
+  // every lane's loads of a split are issued together (J float4 groups, one
+  // row each as MP is a multiple of 4), eight splits at a time
+  constexpr int J = kGramRows * MP / 1024;
+  bool ok[J];
+  double y[J][4];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    ok[j] = rb + (1024 * j + 4 * (int)threadIdx.x) / MP < p;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[j][q] = 0.0;
+  }
+#pragma unroll 8
+  for (int ts = 0; ts < nsplit; ++ts) {
+    float4 v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = 1024 * j + 4 * threadIdx.x;
+      v[j] = ldg_f32x4(Y + ts * stride + (ok[j] ? e : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      y[j][0] += ok[j] ? (double)v[j].x : 0.0;
+      y[j][1] += ok[j] ? (double)v[j].y : 0.0;
+      y[j][2] += ok[j] ? (double)v[j].z : 0.0;
+      y[j][3] += ok[j] ? (double)v[j].w : 0.0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 1024 * j + 4 * threadIdx.x;
+    const float4 f = make_float4((float)y[j][0], (float)y[j][1], (float)y[j][2], (float)y[j][3]);
+    *(float4*)(tile + e) = f;
+    if (ok[j]) stg16(Xo + e, make_uint4(__float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(f.z),
+                                        __float_as_uint(f.w)));
+  }
+  __syncthreads();
+  hpp_gram_tiles<MP>(
+      [&](int row, int c) { return row < p ? (double)tile[(row - rb) * MP + c] : 0.0; }, pv, row0, part);
 }
 
 // The basis of one sample in LDS: the Gram tiles summed from their partials,
@@ -463,12 +548,16 @@ size_t hpp_qr_scratch_bytes(int MP, int B, int p) {
 }
 
 template <int MP>
-static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, float* resid, int ms, char* scratch, const HppNext* next,
-                         hipStream_t s) {
+static hipError_t hpp_qr(const float* Ypart, int nsplit, float* X, int B, int p, int mt, const void* P, int ptype,
+                         float tau, float* W3, int ldw, int32_t* rank, float* resid, int ms, char* scratch,
+                         const HppNext* next, hipStream_t s) {
   const int nparts = (p + kGramRows - 1) / kGramRows;
   double* part = (double*)scratch;
-  hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
+  if (Ypart)
+    hipLaunchKernelGGL(k_hpp_ysum_gram<MP>, dim3(nparts, B), dim3(256), 0, s, Ypart, nsplit, B, X, p, mt, P, ptype,
+                       part);
+  else
+    hipLaunchKernelGGL(k_hpp_gram<MP>, dim3(nparts, B), dim3(256), 0, s, X, p, mt, P, ptype, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   HppNext nx;
@@ -479,13 +568,16 @@ static hipError_t hpp_qr(const float* X, int B, int p, int mt, const void* P, in
   return hipGetLastError();
 }
 
-hipError_t launch_hpp_qr(const float* X, int MP, int B, int p, int mt, const void* P, int ptype, float tau, float* W3,
-                         int ldw, int32_t* rank, float* resid, int ms, void* scratch, const HppNext* next,
-                         hipStream_t s) {
+hipError_t launch_hpp_qr(const float* Ypart, int nsplit, float* X, int MP, int B, int p, int mt, const void* P,
+                         int ptype, float tau, float* W3, int ldw, int32_t* rank, float* resid, int ms, void* scratch,
+                         const HppNext* next, hipStream_t s) {
   if (next && (ldw > MP + kMaxTail || next->ncols > ldw || next->NCB * 16 != ldw)) return hipErrorInvalidValue;
   if (ms < 0 || ms > MP || ms > 256) return hipErrorInvalidValue;
-  if (MP == 16) return hpp_qr<16>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
-  if (MP == 32) return hpp_qr<32>(X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
+  if (Ypart && nsplit < 1) return hipErrorInvalidValue;
+  if (MP == 16)
+    return hpp_qr<16>(Ypart, nsplit, X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
+  if (MP == 32)
+    return hpp_qr<32>(Ypart, nsplit, X, B, p, mt, P, ptype, tau, W3, ldw, rank, resid, ms, (char*)scratch, next, s);
   return hipErrorInvalidValue;
 }
 
