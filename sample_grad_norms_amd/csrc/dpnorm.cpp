@@ -76,6 +76,7 @@ struct PassPlan {
   int NCB = 2, HL = 1;
   int64_t B = 0, T = 0, Tpad = 0;
   int nch = 0, nsplit = 1, cols2 = kColsK2Bf16, rbs = 0;
+  int halves2 = 1;  // 2: stage-2 items of 256 columns on two pairs of waves, one per half of the T split
   int rows1 = kRowsK1;  // rows per stage-1 item
   bool store = false;
   bool fuse = false;            // group layers that share X2
@@ -193,6 +194,18 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
       const int64_t fill = (kMinItems + base_items - 1) / base_items;
       pl.nsplit = std::max(pl.nsplit, (int)std::min<int64_t>(fill, max_small));
     }
+  }
+  // A bf16 call that splits T under 512-column items takes 256-column items
+  // on two pairs of waves, each pair on one half of a split twice as long:
+  // as many work groups of four waves, half the partial tiles to write and
+  // sum. (Only where every group is at most 32 columns wide: the pairs'
+  // stages fill the LDS at that width.)
+  if (pl.bf16 && pl.cols2 == kColsK2Bf16 && pl.nsplit > 1 &&
+      std::all_of(pl.groups.begin(), pl.groups.end(), [](const PassGroup& g) { return g.ncb <= 2; })) {
+    pl.cols2 = kColsK2Bf16Narrow;
+    pl.halves2 = 2;
+    pl.nsplit = (pl.nsplit + 1) / 2;
+    for (PassGroup& g : pl.groups) g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
   }
   // stage-1 items, largest rows first so the launch ends on short items
   std::vector<int> order(nl);
@@ -413,7 +426,8 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {
     st.items = items2 + pl.class_begin[c];
     st.n_items = pl.class_end[c] - pl.class_begin[c];
-    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.cols2, pl.direct(), impl, s));
+    DPN_TRY(launch_tcontract(st, pl.bf16, pl.class_ncb[c], pl.cols2, pl.direct(), impl, s,
+                             pl.class_ncb[c] <= 2 ? pl.halves2 : 1));
     DPN_TRY(tr.mark(DPNORM_KERNEL_TCONTRACT));
     if (pl.needs_ysum() && ysum) {
       DPN_TRY(launch_ysum(st, pl.class_ncb[c], pl.cols2, pl.store ? MODE_STORE : MODE_SQ, impl, s));

@@ -108,8 +108,10 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).
 // cols: columns of X2 per item (kColsK2Bf16 or kColsK2Bf16Narrow for bf16; kColsK2F32).
+// halves = 2: bf16, kColsK2Bf16Narrow, not direct, NCB <= 2: four waves per
+// item, two on each half of the item's T split.
 hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, int cols, bool direct, bool implicit,
-                            hipStream_t s);
+                            hipStream_t s, int halves = 1);
 hipError_t launch_ysum(const StageArgs& a, int NCB, int cols_per_block, int mode, bool implicit, hipStream_t s);
 // work groups of the split-T reduction per (layer, sample, column block)
 inline int ysum_chunks(int cols_per_block, int NCB) { return (cols_per_block * 16 * NCB + kYsumChunk - 1) / kYsumChunk; }

@@ -520,29 +520,41 @@ __device__ __forceinline__ void tcontract_epilogue(const StageArgs& a, const Lay
 // the contraction index runs along the MFMA K slots, and multiplies it
 // against the hi and lo fragments of V. Rows past T and columns past w load
 // the last valid row / column and are zeroed after the LDS read.
+//
+// KT = 2 (two-wave column groups only, T split into partial tiles): two such
+// pairs of waves take the first and the second half of the split's chunks,
+// each stage holding one chunk of each half, and the second pair's
+// accumulators are added to the first's through LDS at the end. A call then
+// needs half the splits (and half the partial tiles) for as many work groups
+// of four waves. When the split has an odd number of chunks, the second
+// pair's last stage reloads the split's last chunk and zeroes it.
 // ---------------------------------------------------------------------------
 constexpr int kK2Rows = 32;                              // rows of X2 per stage (one MFMA K step)
 
 
-template <int NCB, bool DIRECT, bool IMPL, int NW = 4>
-__global__ void __launch_bounds__(64 * NW) k_tcontract_bf16(StageArgs a) {
+template <int NCB, bool DIRECT, bool IMPL, int NW = 4, int KT = 1>
+__global__ void __launch_bounds__(64 * NW * KT) k_tcontract_bf16(StageArgs a) {
   static_assert(NW == 2 || NW == 4, "work groups of two or four waves");
+  static_assert(KT == 1 || (KT == 2 && NW == 2 && !DIRECT), "T halves only for two-wave groups that store tiles");
   constexpr int kCols = 128 * NW;                        // columns of X2 per item
   constexpr int kRowBytes = 2 * kCols;                   // one row of the item in LDS
   constexpr int kRowsPerDma = 1024 / kRowBytes;          // rows per 1 KB load (1 or 2)
   constexpr int kLanesPerRow = kRowBytes / 16;
   constexpr int kK2XBytes = kK2Rows * kRowBytes;         // X2 bytes per stage (32 or 16 KB)
   constexpr int kVBlocks = 2 * NCB;                      // 1 KB V fragment blocks per chunk
-  constexpr int kStage = kK2XBytes + kVBlocks * 1024;
-  constexpr int kBufs = NW == 4 ? (NCB <= 2 ? 4 : 3) : (4 * kStage <= 80 * 1024 ? 4 : 3);  // LDS ring
+  constexpr int kHalf = kK2XBytes + kVBlocks * 1024;     // one chunk and its V blocks
+  constexpr int kStage = KT * kHalf;
+  constexpr int kBufs = NW * KT == 4 ? (NW == 4 ? (NCB <= 2 ? 4 : 3) : (4 * kStage <= 160 * 1024 ? 4 : 3))
+                                     : (4 * kStage <= 80 * 1024 ? 4 : 3);  // LDS ring
   constexpr int kXDma = kK2XBytes / 1024 / NW;           // 1 KB X2 loads per wave per stage (8)
   constexpr int kP = kXDma + kVBlocks / NW;              // loads every wave issues per stage (at least)
+  static_assert(KT == 1 || kBufs * kStage >= NW * 8 * NCB * 4 * 64 * 4, "the ring holds the accumulator exchange");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kBufs * kStage];
   const int4 it = stage2_item<IMPL>(a, xcd_item(blockIdx.x, (uint32_t)a.n_items));
   const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, ub = it.z, ts = it.w;
   const int w = L->w2, T = a.T;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) % NW, wt = (threadIdx.x >> 6) / NW;
   const int n = lane & 15, g = lane >> 4;
   const int wave_u0 = ub * kCols + wv * 128;
   const bool uok = wave_u0 + 8 * n < w;
@@ -553,13 +565,15 @@ __global__ void __launch_bounds__(64 * NW) k_tcontract_bf16(StageArgs a) {
   const uint4* V = (const uint4*)L->V + (int64_t)i * (a.Tpad / 32) * (NCB * 2 * 64) + lane;
   const int nch = (T + 31) >> 5;
   const int c0 = (int)((int64_t)ts * nch / a.nsplit), c1 = (int)((int64_t)(ts + 1) * nch / a.nsplit);
-  const int ncs = c1 - c0;
+  const int ncs = (c1 - c0 + KT - 1) / KT;               // stages (chunks of the first half)
+  // this pair's first chunk, and its number of chunks
+  const int cw = c0 + wt * ncs, nw = KT == 1 ? ncs : (wt == 0 ? ncs : c1 - c0 - ncs);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
   auto dma = [&](int st) {
     if (st >= ncs) return;
-    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage);
-    const int c = c0 + st;
+    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage + wt * kHalf);
+    const int c = st < nw ? cw + st : c1 - 1;   // past this pair's chunks: reloaded, zeroed after the read
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
       int t = kK2Rows * c + (kXDma * wv + j) * kRowsPerDma + drow;
@@ -589,20 +603,24 @@ __global__ void __launch_bounds__(64 * NW) k_tcontract_bf16(StageArgs a) {
     wait_after<kP>(min(kBufs - 2, ncs - 1 - st));
     block_barrier();
     dma(st + kBufs - 1);
-    const unsigned char* buf = lds + (st % kBufs) * kStage;
-    const int t0 = kK2Rows * (c0 + st);
+    const unsigned char* buf = lds + (st % kBufs) * kStage + wt * kHalf;
+    const int t0 = kK2Rows * (cw + st);
+    const bool cok = KT == 1 || st < nw;
     uint4 raw[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int r = slot_row(g, s);
       const uint4 x = *(const uint4*)(buf + r * kRowBytes + wv * 256 + n * 16);
-      raw[s] = (uok && t0 + r < T) ? x : z;
+      raw[s] = (uok && cok && t0 + r < T) ? x : z;
     }
     uint4 bv[NCB][2];
 #pragma unroll
     for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bv[jb][h] = *(const uint4*)(buf + kK2XBytes + (jb * 2 + h) * 1024 + lane * 16);
+      for (int h = 0; h < 2; ++h) {
+        const uint4 v = *(const uint4*)(buf + kK2XBytes + (jb * 2 + h) * 1024 + lane * 16);
+        bv[jb][h] = cok ? v : z;
+      }
     uint4 op[8];
     transpose8x8_bf16(raw, op);
 #pragma unroll
@@ -611,6 +629,27 @@ __global__ void __launch_bounds__(64 * NW) k_tcontract_bf16(StageArgs a) {
       for (int e = 0; e < 8; ++e)
 #pragma unroll
         for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = mfma_bf16(op[e], bv[jb][h], acc[e][jb]);
+  }
+  if constexpr (KT == 2) {
+    // the second pair's sums are added to the first pair's (in that order)
+    float* xch = (float*)lds + (int64_t)wv * (8 * NCB * 4 * 64) + lane;
+    __syncthreads();   // every wave is done with the ring
+    if (wt == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xch[((e * NCB + jb) * 4 + r) * 64] = acc[e][jb][r];
+    }
+    __syncthreads();
+    if (wt == 1) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[e][jb][r] += xch[((e * NCB + jb) * 4 + r) * 64];
   }
   tcontract_epilogue<NCB, 8, DIRECT, NW>(a, L, acc, i, ub, ts, wave_u0, 8, lane, wv);
 }
@@ -813,11 +852,25 @@ hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int ro
 }
 
 hipError_t launch_tcontract(const StageArgs& a, bool bf16, int NCB, int cols, bool direct, bool implicit,
-                            hipStream_t s) {
+                            hipStream_t s, int halves) {
   if (a.n_items <= 0) return hipSuccess;
   if (implicit && (!bf16 || a.ubs < 1 || (NCB != 1 && NCB != 2 && NCB != 4))) return hipErrorInvalidValue;
   if (bf16 && cols != kColsK2Bf16 && cols != kColsK2Bf16Narrow) return hipErrorInvalidValue;
+  if (halves != 1 && (halves != 2 || !bf16 || cols != kColsK2Bf16Narrow || direct || NCB > 2))
+    return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
+  if (halves == 2) {  // two pairs of waves over 256 columns, one half of the split each
+#define DPN_TCH(N, I) hipLaunchKernelGGL((k_tcontract_bf16<N, false, I, 2, 2>), grid, blk, 0, s, a)
+    if (implicit) {
+      if (NCB == 1) DPN_TCH(1, true);
+      else DPN_TCH(2, true);
+    } else {
+      if (NCB == 1) DPN_TCH(1, false);
+      else DPN_TCH(2, false);
+    }
+#undef DPN_TCH
+    return hipGetLastError();
+  }
   if (bf16 && cols == kColsK2Bf16Narrow) {  // two-wave work groups of 256 columns
     const dim3 blk2(128);
 #define DPN_TCN(N, I)                                                                           \

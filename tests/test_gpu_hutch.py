@@ -260,6 +260,20 @@ def test_config3_full_size_stack():
     check(n_all.cpu(), tot, 1e-4, "config3 grouped vs sum of single calls")
 
 
+@pytest.mark.parametrize("B,T,d,p,k", [(4, 8200, 2040, 264, 32), (4, 8232, 2048, 136, 16)])
+def test_stage2_split_halves_shapes(B, T, d, p, k):
+    """Shapes whose 512-column stage-2 items would split T: B * ceil(d/512)
+    = 16 items, 257-258 chunks of 32 rows, 16 splits of at least 512 rows.
+    They take 256-column items on two pairs of waves over 8 splits of 32-33
+    chunks, so in some splits the second pair has one chunk fewer than the
+    first and its last stage is zeroed; T and (first shape) d are ragged."""
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(B, T, d, p, k, seed=71, device=dev(), dtype=torch.bfloat16)
+    n = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    check(n.cpu(), oracle.hutch(prob.A, prob.G, prob.P), TOL[torch.bfloat16], f"halves B{B} T{T} d{d} p{p} k{k}")
+
+
 def test_config5_full_size_hutch():
     import sample_grad_norms_amd as dp
     prob = workloads.config5(device=dev())
