@@ -554,7 +554,9 @@ __global__ void __launch_bounds__(64 * NW * KT) k_tcontract_bf16(StageArgs a) {
   const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, ub = it.z, ts = it.w;
   const int w = L->w2, T = a.T;
-  const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) % NW, wt = (threadIdx.x >> 6) / NW;
+  const int lane = threadIdx.x & 63;
+  const int wv = KT == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) % NW;   // column wave
+  const int wt = KT == 1 ? 0 : (int)(threadIdx.x >> 6) / NW;                         // T half
   const int n = lane & 15, g = lane >> 4;
   const int wave_u0 = ub * kCols + wv * 128;
   const bool uok = wave_u0 + 8 * n < w;
