@@ -235,22 +235,23 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   double (&M)[MP][kMaxTail] = sb.M;
   const int l = threadIdx.x;
   const double* pi = part + (int64_t)i * nparts * NT * 256;
-  // fixed-order sum over the parts (eight at a time, every tile's loads in
-  // flight together); lane q, element j of a v_mfma_f64_16x16x4 result is
+  // fixed-order sum over the parts (sixteen or eight at a time, every tile's
+  // loads in flight together); lane q, element j of a v_mfma_f64_16x16x4 result is
   // (row q/16 + 4 j, column q % 16); thread l holds element l of each tile
+  constexpr int PR = NT <= 3 ? 16 : 8;   // parts whose loads are in flight together
   double v[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) v[t] = 0.0;
-  for (int s0 = 0; s0 < nparts; s0 += 8) {
-    double w[NT][8];
+  for (int s0 = 0; s0 < nparts; s0 += PR) {
+    double w[NT][PR];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[t][u] = pi[(int64_t)min(s0 + u, nparts - 1) * NT * 256 + t * 256 + l];
+      for (int u = 0; u < PR; ++u) w[t][u] = pi[(int64_t)min(s0 + u, nparts - 1) * NT * 256 + t * 256 + l];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[t] += s0 + u < nparts ? w[t][u] : 0.0;
+      for (int u = 0; u < PR; ++u) v[t] += s0 + u < nparts ? w[t][u] : 0.0;
   }
   {
     const int j = l >> 6, q = l & 63;
@@ -282,49 +283,104 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   // minus the squares of the kept rows above it, subtracted in row order.
   // The same row operations on the identity give E = R^-T with its rows left
   // unscaled: row j is scaled by d_j^(-1/2) once at the end (rows of dropped
-  // columns by 0). A step reads only row j, which it never writes, so it
-  // needs one barrier; a thread reads its operands of row j together with
-  // the pivot, and the square roots wait until after the loop (Sc[j][j] keeps
-  // d_j, since later steps change only entries below and right of it).
+  // columns by 0). The square roots wait until after the loop (Sc[j][j]
+  // keeps d_j, since later steps change only entries below and right of it).
   // Column j is kept when d_j^(1/2) > tau max_a ||x_a||, compared as squares.
+  // Steps go in pairs, one barrier each: every thread reads rows j and j + 1
+  // and recomputes the entries of row j + 1 it needs after step j with the
+  // same operations as their owners, then applies both steps to its own
+  // entries, which it holds in registers; it stores those of rows read by
+  // later pairs (rows past j + 1) before the barrier and the rest after the
+  // loop, so no entry of rows j, j + 1 changes while the pair reads them.
   double (&Sc)[MP][MP] = G;
   double (&E)[MP][MP] = Ri;
   double (&sj)[MP] = sb.sj;
   constexpr int EPT = MP * MP / 256;   // entries per thread
+  static_assert(MP % 2 == 0, "steps go in pairs");
   for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
   double dmax = 0.0;
   for (int j = 0; j < MP; ++j) dmax = fmax(dmax, Sc[j][j]);
   const double thr = (double)tau * sqrt(fmax(dmax, 0.0));
   const double thr2 = thr * thr;
   if (l == 0) sb.xmax2 = dmax;
+  double xs[EPT], xe[EPT];   // this thread's entries of Sc and E
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = l + 256 * u;
+    xs[u] = (&Sc[0][0])[e];
+    xe[u] = (e / MP == e % MP) ? 1.0 : 0.0;
+  }
   __syncthreads();
   uint32_t keep = 0;
-  for (int j = 0; j < MP; ++j) {
-    const double dj = Sc[j][j];
-    double sjr[EPT], sjc[EPT], ejc[EPT];
+  for (int j = 0; j < MP; j += 2) {
+    const int j1 = j + 1;
+    const double dj = Sc[j][j], aj1 = Sc[j][j1];
+    double d1 = Sc[j1][j1];
+    double s0r[EPT], s0c[EPT], e0c[EPT], s1r[EPT], s1c[EPT], e1c[EPT];
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
       const int e = l + 256 * u, r = e / MP, c = e % MP;
-      sjr[u] = Sc[j][r];
-      sjc[u] = Sc[j][c];
-      ejc[u] = E[j][c];
+      s0r[u] = Sc[j][r];
+      s0c[u] = Sc[j][c];
+      e0c[u] = E[j][c];
+      s1r[u] = Sc[j1][r];
+      s1c[u] = Sc[j1][c];
+      e1c[u] = E[j1][c];
     }
-    const bool kept = dj > 0.0 && dj > thr2;   // uniform
-    if (kept) {
+    // step j
+    const bool kept0 = dj > 0.0 && dj > thr2;   // uniform
+    if (kept0) {
       keep |= 1u << j;
       const double inv = 1.0 / dj;
+      // row j + 1 after step j, as its owners compute it (their factor is
+      // Sc[j][j+1] / d_j)
+      const double f1 = aj1 * inv;
+      d1 -= f1 * aj1;
 #pragma unroll
       for (int u = 0; u < EPT; ++u) {
         const int e = l + 256 * u, r = e / MP, c = e % MP;
+        if (r > j) s1r[u] -= f1 * s0r[u];
+        if (c > j) s1c[u] -= f1 * s0c[u];
+        e1c[u] -= f1 * e0c[u];
         if (r > j) {
-          const double f = sjr[u] * inv;
-          if (c > j) Sc[r][c] -= f * sjc[u];
-          E[r][c] -= f * ejc[u];
+          const double f = s0r[u] * inv;
+          if (c > j) xs[u] -= f * s0c[u];
+          xe[u] -= f * e0c[u];
         }
+      }
+    }
+    // step j + 1
+    const bool kept1 = d1 > 0.0 && d1 > thr2;   // uniform
+    if (kept1) {
+      keep |= 1u << j1;
+      const double inv = 1.0 / d1;
+#pragma unroll
+      for (int u = 0; u < EPT; ++u) {
+        const int e = l + 256 * u, r = e / MP, c = e % MP;
+        if (r > j1) {
+          const double f = s1r[u] * inv;
+          if (c > j1) xs[u] -= f * s1c[u];
+          xe[u] -= f * e1c[u];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = l + 256 * u, r = e / MP;
+      if (r > j1) {
+        (&Sc[0][0])[e] = xs[u];
+        (&E[0][0])[e] = xe[u];
       }
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = l + 256 * u;
+    (&Sc[0][0])[e] = xs[u];
+    (&E[0][0])[e] = xe[u];
+  }
+  __syncthreads();
   if (l < MP) sj[l] = (keep >> l) & 1u ? 1.0 / sqrt(Sc[l][l]) : 0.0;
   __syncthreads();
   for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] *= sj[e / MP];
