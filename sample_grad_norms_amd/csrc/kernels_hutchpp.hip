@@ -216,7 +216,6 @@ __global__ void __launch_bounds__(256) k_hpp_ysum_gram(const float* __restrict__
 template <int MP>
 struct HppBasis {
   double G[MP][MP], XP[MP][kMaxTail], R[MP][MP], Ri[MP][MP], M[MP][kMaxTail], N[MP][kMaxTail];
-  double sj[MP];   // 1 / R[j][j] of kept columns, 0 of dropped ones
   double xmax2;    // the largest squared column norm of X
 };
 
@@ -293,8 +292,7 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
   // later pairs (rows past j + 1) before the barrier and the rest after the
   // loop, so no entry of rows j, j + 1 changes while the pair reads them.
   double (&Sc)[MP][MP] = G;
-  double (&E)[MP][MP] = Ri;
-  double (&sj)[MP] = sb.sj;
+  double (&E)[MP][MP] = R;
   constexpr int EPT = MP * MP / 256;   // entries per thread
   static_assert(MP % 2 == 0, "steps go in pairs");
   for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] = (e / MP == e % MP) ? 1.0 : 0.0;
@@ -381,14 +379,13 @@ __device__ uint32_t hpp_basis(const double* __restrict__ part, int nparts, float
     (&E[0][0])[e] = xe[u];
   }
   __syncthreads();
-  if (l < MP) sj[l] = (keep >> l) & 1u ? 1.0 / sqrt(Sc[l][l]) : 0.0;
-  __syncthreads();
-  for (int e = l; e < MP * MP; e += 256) (&E[0][0])[e] *= sj[e / MP];
-  __syncthreads();
-  // Ri = E^T, back into Ri's storage (E aliases it): transpose via R (scratch)
-  for (int e = l; e < MP * MP; e += 256) (&R[0][0])[e] = E[e % MP][e / MP];
-  __syncthreads();
-  for (int e = l; e < MP * MP; e += 256) (&Ri[0][0])[e] = (&R[0][0])[e];
+  // Ri = E^T with row c of E (held in R) scaled by d_c^(-1/2), 0 for dropped
+  // columns; every thread takes the square roots it needs itself
+  for (int e = l; e < MP * MP; e += 256) {
+    const int a = e / MP, c = e % MP;
+    const double sc = (keep >> c) & 1u ? 1.0 / sqrt(Sc[c][c]) : 0.0;
+    (&Ri[0][0])[e] = E[c][a] * sc;
+  }
   __syncthreads();
   // M[c][t] = sum_a Ri[a][c] XP[a][t]
   // (both sums run over the triangle of Ri in index order; every operand is
