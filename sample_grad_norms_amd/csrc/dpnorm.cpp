@@ -78,6 +78,7 @@ struct PassPlan {
   int nch = 0, nsplit = 1, cols2 = kColsK2Bf16, rbs = 0;
   int halves2 = 1;  // 2: stage-2 items of 256 columns on two pairs of waves, one per half of the T split
   int rows1 = kRowsK1;  // rows per stage-1 item
+  int ks1 = 1;          // 2: 64-row items on four waves that split the columns in two
   bool store = false;
   bool fuse = false;            // group layers that share X2
   size_t off_recs = 0, off_items1 = 0, off_items2 = 0, off_partials = 0;
@@ -154,6 +155,10 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
   pl.rows1 = kRowsK1;
   if (pl.bf16 && items128 < kMinItems)
     pl.rows1 = 2 * items128 < kMinItems && pl.NCB * pl.HL <= 2 ? kRowsK1Tiny : kRowsK1Small;
+  // 64-row items that fit the CUs in one round, one work group each, take
+  // four waves: two per 32-row group, each streaming every other column
+  // chunk (where two-wave groups could run two to a CU, they keep two waves)
+  if (pl.bf16 && pl.rows1 == kRowsK1Small && pl.NCB * pl.HL <= 4 && 2 * items128 <= kMinItems) pl.ks1 = 2;
   pl.rbs = (int)(pl.Tpad / pl.rows1);
   pl.cols2 = pl.bf16 ? kColsK2Bf16 : kColsK2F32;
   form_groups(pl, L);
@@ -420,7 +425,7 @@ hipError_t run_pass(const PassPlan& pl, const std::vector<PassLayer>& L, char* b
 
   st.items = items1;
   st.n_items = (int32_t)pl.total1;
-  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, raw, impl, s));
+  DPN_TRY(launch_rowproj(st, pl.bf16, pl.NCB, pl.HL, pl.rows1, raw, impl, s, pl.ks1));
   DPN_TRY(tr.mark(DPNORM_KERNEL_ROWPROJ));
 
   for (size_t c = 0; c < pl.class_ncb.size(); ++c) {

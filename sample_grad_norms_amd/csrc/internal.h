@@ -102,8 +102,10 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
 // raw: every record's W is the caller's bf16 [w1][16 NCB] matrix, read in
 // place (bf16, HL == 1 only); implicit: the stages run in implicit mode
 // (which reads W in place too).
+// ks1 = 2 (bf16, rows1 == kRowsK1Small, NCB HL <= 4): the 64-row items on
+// four waves, two per 32-row group, each streaming every other column chunk.
 hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool raw, bool implicit,
-                          hipStream_t s);
+                          hipStream_t s, int ks1 = 1);
 // direct = 1: nsplit == 1 and mode SQ, partial sums are written by the stage
 // itself; otherwise Y partial tiles go to Ypart and launch_ysum finishes them.
 // NCB in {1, 2, 3, 4, 6}: the column blocks of V (those of every projection of a group).

@@ -214,12 +214,14 @@ constexpr int kK1XDma = 32 * kK1Cols * 2 / 1024;     // 1 KB X1 instructions per
 constexpr int kK1Bufs = 4;                           // LDS ring: three stages in flight, one in use
 
 // NW waves. KS = 1: wave w owns rows 32 w .. 32 w + 31 of a 32 NW-row item
-// (128 rows normally, 64 when 128-row items would leave CUs idle). KS = NW
-// (K split, for calls with fewer items still): all waves share one 32-row
-// item and stage st holds NW consecutive 64-column chunks of it, one per
-// wave (chunk NW st + w, counted from the group's first chunk), each with its
-// 64 rows of W; at the end the waves' partial sums are added through LDS in
-// wave order, so the result does not depend on timing.
+// (128 rows normally, 64 when 128-row items would leave CUs idle). KS > 1
+// (K split): the item has 32 NW / KS rows, wave w takes 32-row group w / KS
+// of it, and stage st holds KS consecutive 64-column chunks, one per K slot
+// (chunk KS st + w % KS, counted from the group's first chunk), each with
+// its 64 rows of W; at the end the partial sums of K slots 1 .. KS - 1 are
+// added to slot 0's through LDS in slot order, so the result does not depend
+// on timing. KS = NW: one 32-row item for all waves (calls with few items);
+// KS = 2 with four waves: 64-row items with two waves' loads per row group.
 // RAW (HL = 1): W is the caller's bf16 [w1][NC] matrix. A chunk's 64 rows
 // of it are one contiguous run, loaded as they are (rows past w1 from a zero
 // row) and kept row-major in LDS; each B operand is two transposing reads
@@ -230,7 +232,7 @@ template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
 __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   static_assert(!RAW || HL == 1, "W read in place is bf16");
   static_assert(!IMPL || RAW, "implicit mode reads W in place");
-  static_assert(KS == 1 || KS == NW, "the K split spreads one 32-row item over all waves");
+  static_assert(NW % KS == 0, "the K split spreads each 32-row group over KS waves");
   constexpr int NC = 16 * NCB;
   constexpr int kRows = 32 * NW / KS;                    // rows per item
   constexpr int kK1XBytes = NW * 32 * kK1Cols * 2;       // X1 bytes per stage (16 KB for 4 waves)
@@ -244,8 +246,8 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   const int i = it.y, rb = it.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int rg = KS == 1 ? wv : 0;                       // this wave's 32-row group within the item
-  const int kq = KS == 1 ? 0 : wv;                       // this wave's chunk within a stage
+  const int rg = KS == 1 ? wv : wv / KS;                 // this wave's 32-row group within the item
+  const int kq = KS == 1 ? 0 : wv % KS;                  // this wave's chunk within a stage
   const int w = L->w1, T = a.T;
   const int r0 = rb * kRows;
   const uint16_t* X = (const uint16_t*)L->X1 + (int64_t)i * T * w;
@@ -352,21 +354,21 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   }
 
   if (KS > 1) {
-    // partial sums of waves 1 .. KS - 1 through LDS (every wave is past its
-    // last LDS read once all have reached this barrier), added by wave 0 in
-    // wave order
+    // partial sums of K slots 1 .. KS - 1 through LDS (every wave is past its
+    // last LDS read once all have reached this barrier), added by the row
+    // group's slot-0 wave in slot order
     block_barrier();
-    float* red = (float*)lds;
-    if (wv > 0) {
+    float* red = (float*)lds + rg * (KS - 1) * (2 * NCB * 256);
+    if (kq > 0) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int jb = 0; jb < NCB; ++jb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) red[(((wv - 1) * 2 + mt) * NCB + jb) * 256 + r * 64 + lane] = acc[mt][jb][r];
+          for (int r = 0; r < 4; ++r) red[(((kq - 1) * 2 + mt) * NCB + jb) * 256 + r * 64 + lane] = acc[mt][jb][r];
     }
     __syncthreads();
-    if (wv > 0) return;
+    if (kq > 0) return;
 #pragma unroll
     for (int q = 1; q < KS; ++q)
 #pragma unroll
@@ -814,7 +816,8 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
 // (the host takes 64-row items for wider W), so no other is instantiated.
 template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
 static void rowproj_bf16_one(const StageArgs& a, hipStream_t s) {
-  if constexpr (KS == 1 || NCB * HL <= 2)
+  // only the forms whose stage ring fits the LDS (the host asks for no other)
+  if constexpr (kK1Bufs * (NW * 32 * kK1Cols * 2 + KS * 2 * NCB * HL * 1024) <= 160 * 1024)
     hipLaunchKernelGGL((k_rowproj_bf16<NCB, HL, NW, RAW, IMPL, KS>), dim3(a.n_items), dim3(64 * NW), 0, s, a);
 }
 
@@ -834,13 +837,15 @@ static void rowproj_bf16_nw(const StageArgs& a, int NCB, int HL, bool raw, bool 
 }
 
 hipError_t launch_rowproj(const StageArgs& a, bool bf16, int NCB, int HL, int rows1, bool raw, bool implicit,
-                          hipStream_t s) {
+                          hipStream_t s, int ks1) {
   if (a.n_items <= 0) return hipSuccess;
   if ((raw || implicit) && (!bf16 || HL != 1)) return hipErrorInvalidValue;
   if (implicit && a.rbs < 1) return hipErrorInvalidValue;
   const dim3 grid(a.n_items), blk(256);
   if (bf16) {
+    if (ks1 != 1 && (ks1 != 2 || rows1 != kRowsK1Small || NCB * HL > 4)) return hipErrorInvalidValue;
     if (rows1 == kRowsK1) rowproj_bf16_nw<4, 1>(a, NCB, HL, raw, implicit, s);
+    else if (rows1 == kRowsK1Small && ks1 == 2) rowproj_bf16_nw<4, 2>(a, NCB, HL, raw, implicit, s);
     else if (rows1 == kRowsK1Small) rowproj_bf16_nw<2, 1>(a, NCB, HL, raw, implicit, s);
     else if (rows1 == kRowsK1Tiny && NCB * HL <= 2) rowproj_bf16_nw<4, 4>(a, NCB, HL, raw, implicit, s);
     else return hipErrorInvalidValue;
