@@ -260,6 +260,19 @@ def test_config3_full_size_stack():
     check(n_all.cpu(), tot, 1e-4, "config3 grouped vs sum of single calls")
 
 
+@pytest.mark.parametrize("B,T,d,p,k", [(2, 8192, 264, 520, 32), (1, 16320, 136, 1000, 64)])
+def test_stage1_two_k_slots_shapes(B, T, d, p, k):
+    """Shapes with exactly 128 stage-1 items of 128 rows: they take 64-row
+    items on four waves, two per 32-row group, each streaming every other
+    64-column chunk of G (p ragged against the 64-column chunks; k = 32 with P
+    read in place, k = 64 with four column blocks; T ragged in the second)."""
+    import sample_grad_norms_amd as dp
+    prob = workloads.random_problem(B, T, d, p, k, seed=73, device=dev(), dtype=torch.bfloat16)
+    n = dp.hutch(prob.A, prob.G, prob.P)
+    torch.cuda.synchronize()
+    check(n.cpu(), oracle.hutch(prob.A, prob.G, prob.P), TOL[torch.bfloat16], f"two K slots B{B} T{T} d{d} p{p} k{k}")
+
+
 @pytest.mark.parametrize("B,T,d,p,k", [(4, 8200, 2040, 264, 32), (4, 8232, 2048, 136, 16)])
 def test_stage2_split_halves_shapes(B, T, d, p, k):
     """Shapes whose 512-column stage-2 items would split T: B * ceil(d/512)
