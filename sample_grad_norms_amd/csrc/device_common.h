@@ -163,6 +163,30 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
                "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
+// Same, past this CU's L1 (sc0): the data comes from the XCD's L2, where
+// another CU of the same XCD has just stored it.
+__device__ __forceinline__ void dma16_l2(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc0" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+// A 32-bit counter read with a returning atomic add of 0: performed where
+// the counter's atomic increments are (written out because the compiler
+// would turn an atomic add of 0 into a load, and atomic loads skip the L2
+// that holds the increments), then waited for.
+__device__ __forceinline__ uint32_t atomic_read_u32(uint32_t* p) {
+  uint32_t v;
+  const uint32_t zero = 0u;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=&v"(v) : "v"(p), "v"(zero) : "memory");
+  return v;
+}
+// Two doubles read past this CU's L1 (sc0), both loads in flight, then waited for.
+__device__ __forceinline__ void ldg2_f64_l2(const double* p0, const double* p1, double& a, double& b) {
+  asm volatile("global_load_dwordx2 %0, %2, off sc0\n\tglobal_load_dwordx2 %1, %3, off sc0\n\ts_waitcnt vmcnt(0)"
+               : "=&v"(a), "=&v"(b)
+               : "v"(p0), "v"(p1)
+               : "memory");
+}
 // Work-group barrier that the compiler may not move memory accesses across.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 

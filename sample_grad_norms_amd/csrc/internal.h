@@ -122,6 +122,35 @@ hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, floa
                          float* head, float* tail, float* c, float C, int with_clip, double scale, hipStream_t s);
 hipError_t launch_clip(const float* n, int32_t B, float C, float* c, hipStream_t s);
 
+// One-launch Hutchinson call over one bf16 layer whose P is read in place
+// (k = 16 or 32), for calls too small to fill the GPU with separate stage
+// launches. Sample i belongs to XCD i % 8: that XCD's work groups take
+// tickets in order from its counter, first the sample's stage-1 items (32
+// rows of G each, the four-wave K split of stage 1), then its stage-2 items
+// (64 columns of A over all of T, four waves on the quarters of T, squares
+// summed in the item). The stage-2 items of a sample wait (bounded) until
+// its stage-1 items are done; V and the items' sums pass between the work
+// groups of one XCD through that XCD's L2; the last stage-2 item of a sample
+// sums the items' sums in item order and writes n (and c).
+struct XcdArgs {
+  StageArgs st;            // stage 1 in implicit mode: rec0 = (G, P in place, V), T, Tpad
+  const uint16_t* A;       // [B][T][d]
+  double* sums;            // [B][n2] stage-2 item sums
+  uint32_t* ctr;           // [8] tickets, [B] stage-1 items done, [B] stage-2 items done, [1] timeouts
+  float* n;                // [B]
+  float* c;                // [B] or null
+  float C;
+  int32_t accumulate;
+  int32_t B, d, n1, n2;    // n1 = ceil(T / 32), n2 = ceil(d / 64)
+  uint32_t spin_limit;     // polls of a stage-2 item's wait before it gives up (n = NaN)
+};
+constexpr int kXcdWaves = 4;
+// counters of one call: 8 + 2 B + 1 words
+inline int64_t xcd_counters(int64_t B) { return 8 + 2 * B + 1; }
+// Two launches: a small kernel that zeroes the counters (no memset, so a
+// caller may capture the call in a graph), then the call's kernel.
+hipError_t launch_hutch_xcd(const XcdArgs& x, int NCB, hipStream_t s);
+
 // Hutch++: orthonormal basis Q of the sketch X [B][p][MP] (MP = 16 or 32
 // columns, zero past m_s; dropped columns give zero columns of Q) and
 // P' = P - Q (Q^T P), written as W3 [B][p][ldw] = [Q (MP columns) | P' (mt

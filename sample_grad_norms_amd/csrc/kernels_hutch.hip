@@ -228,8 +228,17 @@ constexpr int kK1Bufs = 4;                           // LDS ring: three stages i
 // (rows 32 kk + 8 g .. + 3 and + 4 .. + 7 of column 16 jb + n), so the call
 // needs no packed copy of W. IMPL: implicit mode (items and record not in
 // memory; always RAW).
+template <int NCB, int HL, int NW, int KS>
+constexpr int rowproj_lds_bytes() {   // the stage ring of one work group
+  return kK1Bufs * (NW * 32 * kK1Cols * 2 + KS * 2 * NCB * HL * 1024);
+}
+
+// One stage-1 item it = (layer, sample, row block) on the work group's LDS
+// ring lds (rowproj_lds_bytes, 1 KB aligned); key picks the first column
+// chunk (work groups start at different chunks). Every wave of the group
+// calls it; waves other than a K split's slot 0 return before the store.
 template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
-__global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
+__device__ __forceinline__ void rowproj_bf16_item(const StageArgs& a, const int4 it, uint32_t key, unsigned char* lds) {
   static_assert(!RAW || HL == 1, "W read in place is bf16");
   static_assert(!IMPL || RAW, "implicit mode reads W in place");
   static_assert(NW % KS == 0, "the K split spreads each 32-row group over KS waves");
@@ -239,9 +248,8 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   constexpr int kWBlocks = 2 * NCB * HL;                 // 1 KB W fragment blocks per chunk
   constexpr int kStage = kK1XBytes + KS * kWBlocks * 1024;
   constexpr int kPerWave = kK1XDma + KS * kWBlocks / NW; // loads every wave issues per stage (at least)
+  static_assert(kK1Bufs * kStage == rowproj_lds_bytes<NCB, HL, NW, KS>(), "ring size");
   static_assert(kK1Bufs * kStage <= 160 * 1024, "the stage ring must fit the LDS of one work group");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kK1Bufs * kStage];
-  const int4 it = stage1_item<IMPL>(a, blockIdx.x);
   const LayerRec* L = layer_rec<IMPL>(a, it.x);
   const int i = it.y, rb = it.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -255,7 +263,7 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
   const uint16_t* Wr = (const uint16_t*)L->W;                       // RAW: [w][NC] as the caller holds it
   const int nch = (w + kK1Cols - 1) / kK1Cols;                      // 64-column chunks
   const int nst = (nch + KS - 1) / KS;
-  const int rot = (int)((blockIdx.x >> 3) * 41u % (unsigned)nch);   // first chunk of this group
+  const int rot = (int)((key >> 3) * 41u % (unsigned)nch);          // first chunk of this group
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
   // X1 source of this lane: instruction j of wave wv fills LDS rows
@@ -389,6 +397,12 @@ __global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
     stg16(out + (jb * 2 + 0) * 64, pack8(hi));
     stg16(out + (jb * 2 + 1) * 64, pack8(lo));
   }
+}
+
+template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
+__global__ void __launch_bounds__(64 * NW) k_rowproj_bf16(StageArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[rowproj_lds_bytes<NCB, HL, NW, KS>()];
+  rowproj_bf16_item<NCB, HL, NW, RAW, IMPL, KS>(a, stage1_item<IMPL>(a, blockIdx.x), blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -804,6 +818,243 @@ __global__ void __launch_bounds__(256) k_clip(const float* n, int32_t B, float C
 }
 
 // ---------------------------------------------------------------------------
+// One-launch Hutchinson over one layer, samples assigned to XCDs.
+//
+// Coherence: the L2 of an XCD serves all of its CUs, and the vector L1 is
+// write-through. A producer's V and item sums are plain stores; it waits
+// until they are acknowledged (vmcnt 0) before it bumps its sample's counter
+// with an agent-scope atomic. A consumer on the same XCD polls that counter
+// with atomic read-modify-writes (adding 0), which are performed where the
+// increments are, and then reads the data past its own L1 (sc0) from the
+// shared L2. No work group waits on a work group of another XCD, so
+// no L2 has to be written back. Tickets are taken in order, and a stage-2
+// item waits only on stage-1 items of lower tickets, which running work
+// groups hold and finish without waiting: the scheme cannot deadlock,
+// whatever the dispatch; the waits are bounded all the same.
+// ---------------------------------------------------------------------------
+
+// 8 rows x 4 columns of bf16 (row s: columns 0, 1 in word x, 2, 3 in word y)
+// to 4 operands of 8 rows each (column e's rows 0..7, row 0 in the low half of
+// word 0).
+__device__ __forceinline__ void transpose8x4_bf16(const uint2 in[8], uint4 out[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = (e < 2) ? in[2 * k].x : in[2 * k].y;
+      const uint32_t b = (e < 2) ? in[2 * k + 1].x : in[2 * k + 1].y;
+      w[k] = (e & 1) ? pack_hi16(a, b) : pack_lo16(a, b);
+    }
+    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Stage 2 of the one-launch call: the sum of squares of Y = X2^T V over the
+// columns u0 .. u0 + 63 of one sample's X2 [T][w] and all of T. Wave q takes
+// the q-th quarter of the 32-row chunks, streamed through an LDS ring as the
+// stage kernels do (its chunk's rows of 128 bytes and its V blocks, read
+// past L1); a lane reads 8 rows of its 4 consecutive columns and transposes
+// them so T runs along the MFMA K slots. The quarters' accumulators are added
+// to wave 0's in wave order through LDS. Returns the sum in thread 0.
+template <int NCB>
+__device__ double tcontract64_item(const uint16_t* X2, const uint4* Vs, int T, int w, int u0, unsigned char* lds) {
+  constexpr int kXBytes = 32 * 128;               // one chunk of 64 columns
+  constexpr int kVBlocks = 2 * NCB;               // 1 KB V blocks per chunk
+  constexpr int kWave = kXBytes + kVBlocks * 1024;
+  constexpr int kStage = kXcdWaves * kWave;
+  constexpr int kBufs = 4;
+  constexpr int kP = 4 + kVBlocks;                // loads every wave issues per stage
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int nch = (T + 31) >> 5;
+  const int ncs = (nch + kXcdWaves - 1) / kXcdWaves;          // stages
+  const int cw = wv * ncs, nw = max(0, min(ncs, nch - cw));   // this wave's first chunk, and its chunks
+  const bool uok = u0 + 4 * n < w;                            // w is a multiple of 8
+  const uint16_t* X = X2 + min(u0 + 8 * (lane & 7), w - 8);   // this lane's 16 bytes of a row
+  const int drow = lane >> 3;                                 // and its row within a 1 KB load
+  const uint4* V = Vs + lane;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+
+  auto dma = [&](int st) {
+    if (st >= ncs) return;
+    const uint32_t buf = lds_base + (uint32_t)((st % kBufs) * kStage + wv * kWave);
+    const int c = st < nw ? cw + st : nch - 1;   // past this quarter's chunks: reloaded, zeroed after the read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = min(32 * c + 8 * j + drow, T - 1);
+      dma16_stream(X + (int64_t)t * w, buf + (uint32_t)(j * 1024));
+    }
+#pragma unroll
+    for (int m = 0; m < kVBlocks; ++m) dma16_l2(V + ((int64_t)c * kVBlocks + m) * 64, buf + (uint32_t)(kXBytes + m * 1024));
+  };
+
+  f32x4_t acc[4][NCB];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint2 z2 = make_uint2(0, 0);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int st = 0; st < kBufs - 1; ++st) dma(st);
+  for (int st = 0; st < ncs; ++st) {
+    wait_after<kP>(min(kBufs - 2, ncs - 1 - st));
+    block_barrier();
+    dma(st + kBufs - 1);
+    const unsigned char* buf = lds + (st % kBufs) * kStage + wv * kWave;
+    const int t0 = 32 * (cw + st);
+    const bool cok = st < nw;
+    uint2 raw[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int r = slot_row(g, s);
+      const uint2 x = *(const uint2*)(buf + r * 128 + n * 8);
+      raw[s] = (uok && cok && t0 + r < T) ? x : z2;
+    }
+    uint4 bv[NCB][2];
+#pragma unroll
+    for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 v = *(const uint4*)(buf + kXBytes + (jb * 2 + h) * 1024 + lane * 16);
+        bv[jb][h] = cok ? v : z;
+      }
+    uint4 op[4];
+    transpose8x4_bf16(raw, op);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb) acc[e][jb] = mfma_bf16(op[e], bv[jb][h], acc[e][jb]);
+  }
+  // quarters 1..3 added to quarter 0 in that order, then the squares
+  __syncthreads();   // every wave is done with the ring
+  float* xch = (float*)lds + lane;
+  if (wv > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xch[((((wv - 1) * 4 + e) * NCB + jb) * 4 + r) * 64] = acc[e][jb][r];
+  }
+  __syncthreads();
+  double sum = 0.0;
+  if (wv == 0) {
+#pragma unroll
+    for (int q = 0; q < kXcdWaves - 1; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[e][jb][r] += xch[(((q * 4 + e) * NCB + jb) * 4 + r) * 64];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int jb = 0; jb < NCB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double y = (double)acc[e][jb][r];
+          sum += y * y;
+        }
+    sum = wave_sum(sum);
+  }
+  return sum;
+}
+
+template <int NCB>
+constexpr int xcd_lds_bytes() {
+  constexpr int s1 = rowproj_lds_bytes<NCB, 1, kXcdWaves, kXcdWaves>();
+  constexpr int s2 = 4 * kXcdWaves * (32 * 128 + 2 * NCB * 1024);
+  return s1 > s2 ? s1 : s2;
+}
+
+__global__ void __launch_bounds__(256) k_xcd_reset(uint32_t* ctr, int32_t words) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < words) ctr[i] = 0u;
+}
+
+template <int NCB>
+__global__ void __launch_bounds__(64 * kXcdWaves) k_hutch_xcd(XcdArgs x) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[xcd_lds_bytes<NCB>()];
+  __shared__ int s_ticket, s_ok;
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  xcc &= 7u;
+  const int B = x.B, n1 = x.n1, n2 = x.n2, per = n1 + n2;
+  const int mine = ((int)B - (int)xcc + 7) / 8;   // samples xcc, xcc + 8, ...
+  uint32_t* ticket = x.ctr + xcc;
+  uint32_t* done1 = x.ctr + 8;
+  uint32_t* done2 = x.ctr + 8 + B;
+  uint32_t* timeouts = x.ctr + 8 + 2 * B;
+  const int T = x.st.T, Tpad = x.st.Tpad, d = x.d;
+  for (;;) {
+    if (threadIdx.x == 0) s_ticket = (int)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = s_ticket;
+    __syncthreads();
+    if (t >= mine * per) break;   // uniform
+    const int s = (int)xcc + 8 * (t / per), r = t % per;
+    if (r < n1) {
+      rowproj_bf16_item<NCB, 1, kXcdWaves, true, true, kXcdWaves>(x.st, make_int4(0, s, r, 0), (uint32_t)t, lds);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's V stores have reached L2
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(done1 + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    if (threadIdx.x == 0) {   // the sample's stage 1, with a bounded wait
+      uint32_t polls = 0;
+      int ok = 1;
+      while (atomic_read_u32(done1 + s) < (uint32_t)n1) {
+        if (++polls > x.spin_limit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      s_ok = ok;
+    }
+    __syncthreads();
+    if (!s_ok) {   // uniform: the sample's estimate is marked invalid and this work group stops
+      if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        x.n[s] = __int_as_float(0x7fc00000);
+        if (x.c) x.c[s] = __int_as_float(0x7fc00000);
+      }
+      break;
+    }
+    const int item = r - n1;
+    const uint16_t* X2 = x.A + (int64_t)s * T * d;
+    const uint4* Vs = (const uint4*)x.st.rec0.V + (int64_t)s * (Tpad / 32) * (NCB * 2 * 64);
+    const double sum = tcontract64_item<NCB>(X2, Vs, T, d, 64 * item, lds);
+    if (threadIdx.x == 0) {
+      x.sums[(int64_t)s * n2 + item] = sum;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the sum has reached L2
+      s_ticket = (int)__hip_atomic_fetch_add(done2 + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_ticket == n2 - 1 && threadIdx.x < 64) {   // the sample's last item: wave 0 sums the items' sums
+      // (lane j the items j and j + 64, read past L1; then a fixed tree over the lanes)
+      const double* sp = x.sums + (int64_t)s * n2;
+      const int j0 = threadIdx.x, j1 = threadIdx.x + 64;
+      double v0, v1;
+      ldg2_f64_l2(sp + min(j0, n2 - 1), sp + min(j1, n2 - 1), v0, v1);
+      double tot = (j0 < n2 ? v0 : 0.0) + (j1 < n2 ? v1 : 0.0);
+      tot = wave_sum(tot);
+      if (threadIdx.x == 0) {
+        const float nv = (float)(x.accumulate ? (double)x.n[s] + tot : tot);
+        x.n[s] = nv;
+        if (x.c) x.c[s] = clip_value(nv, x.C);
+      }
+    }
+    __syncthreads();   // the ring, the exchange area and s_ticket are free for the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
@@ -817,7 +1068,7 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
 template <int NCB, int HL, int NW, bool RAW, bool IMPL, int KS>
 static void rowproj_bf16_one(const StageArgs& a, hipStream_t s) {
   // only the forms whose stage ring fits the LDS (the host asks for no other)
-  if constexpr (kK1Bufs * (NW * 32 * kK1Cols * 2 + KS * 2 * NCB * HL * 1024) <= 160 * 1024)
+  if constexpr (rowproj_lds_bytes<NCB, HL, NW, KS>() <= 160 * 1024)
     hipLaunchKernelGGL((k_rowproj_bf16<NCB, HL, NW, RAW, IMPL, KS>), dim3(a.n_items), dim3(64 * NW), 0, s, a);
 }
 
@@ -952,6 +1203,19 @@ hipError_t launch_finish(const double2* partials, int32_t B, int32_t slots, floa
                          float* tail, float* c, float C, int with_clip, double scale, hipStream_t s) {
   hipLaunchKernelGGL(k_finish, dim3(B), dim3(256), 0, s, partials, slots, n, accumulate, head, tail, c, C,
                      with_clip, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_hutch_xcd(const XcdArgs& x, int NCB, hipStream_t s) {
+  if (x.B < 1 || x.n1 < 1 || x.n2 < 1 || (NCB != 1 && NCB != 2)) return hipErrorInvalidValue;
+  const int words = (int)xcd_counters(x.B);
+  hipLaunchKernelGGL(k_xcd_reset, dim3((words + 255) / 256), dim3(256), 0, s, x.ctr, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // one work group per CU of each XCD (a multiple of 8 keeps the dispatch even)
+  const dim3 grid(256), blk(64 * kXcdWaves);
+  if (NCB == 1) hipLaunchKernelGGL(k_hutch_xcd<1>, grid, blk, 0, s, x);
+  else hipLaunchKernelGGL(k_hutch_xcd<2>, grid, blk, 0, s, x);
   return hipGetLastError();
 }
 
