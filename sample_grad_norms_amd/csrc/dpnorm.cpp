@@ -212,6 +212,13 @@ void plan_pass(PassPlan& pl, const std::vector<PassLayer>& L, Bump& bump) {
     pl.halves2 = 2;
     pl.nsplit = (pl.nsplit + 1) / 2;
     for (PassGroup& g : pl.groups) g.ubs = (int)((L[g.members[0]].w2 + pl.cols2 - 1) / pl.cols2);
+  } else if (pl.bf16 && pl.cols2 == kColsK2Bf16Narrow && pl.nsplit > 1 && pl.nch / pl.nsplit >= kMinChunksPerSplit &&
+             std::all_of(pl.groups.begin(), pl.groups.end(), [](const PassGroup& g) { return g.ncb <= 2; })) {
+    // 256-column items whose splits keep at least 512 rows take the two
+    // pairs of waves too, with the same splits: each pair streams half of
+    // the item's rows (Hutch++ B=4, T=4096, d=p=2048: 130.4-132.4 us ->
+    // 129.8-131.4 us; with 256-row splits the halves were slower)
+    pl.halves2 = 2;
   }
   // stage-1 items, largest rows first so the launch ends on short items
   std::vector<int> order(nl);
